@@ -1,0 +1,192 @@
+/*
+ * spear.h - C ABI of libspear, the compensated 4-bit linear layer on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer computes, per token m (one row of x),
+ *
+ *     y[m] = dequant(W_q) x[m] + g(x[m]) * B (A x[m]),
+ *     g(x) = sigmoid(w_g . x + b_g),
+ *
+ * where dequant(W_q)[n][k] = (q[n][k] - z[n][k/G]) * s[n][k/G] is the 4-bit
+ * weight with fp16 scale s and zero-point z per output row and group of G
+ * input columns, and A (r x K), B (N x r) form a low-rank error compensator.
+ *
+ * Source: "SPEAR: A System for Post-Quantization Error-Adaptive Recovery
+ * Enabling Efficient Low-Bit LLM Serving", explanation pages on gist.science
+ * (paper 2606.11244), English page, Technical Summary:
+ *   - 2.1 A "Input-Adaptive Error Compensators": the compensator projects x
+ *     to rank r with A, applies an input-dependent gate and projects back
+ *     with B; the effective weight is W + alpha B diag(gamma(Ax)) A.  This
+ *     library takes W as the dequantized 4-bit weight, alpha = 1 (folded into
+ *     B) and the gate as one scalar per token, sigmoid(w_g . x + b_g).
+ *   - 2.2 A "Phase-Aware Adaptive Kernel Fusion Dispatch": decode (few
+ *     tokens, memory-bound) runs the compensator inside the low-bit product
+ *     kernel; prefill (many tokens, compute-bound) runs it as a separate
+ *     kernel that overlaps the product.
+ *   - 2.2 C "SLO-Constrained EC-Aware Chunk Scheduling": pick the largest
+ *     prefill chunk whose table-predicted latency meets the latency target.
+ *
+ * Conventions shared by every call:
+ *   - Device pointers are HIP device memory owned by the caller.  The library
+ *     allocates no device memory and copies nothing between host and device.
+ *   - Every compute call is asynchronous on the stream(s) it is given and
+ *     never synchronises.  A stream argument is a hipStream_t passed as a
+ *     void pointer; NULL is the null stream.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     any error nothing is launched, the outputs are untouched and
+ *     spear_last_error() describes the problem for the calling thread.
+ *   - y must not alias any input.
+ *   - Element types: x, y, A, B and w_g share the activation type
+ *     (SPEAR_F16 or SPEAR_BF16); scales and zero-points are always fp16.
+ *     Arithmetic is fp32 throughout; only y is rounded (round to nearest
+ *     even) to the activation type.
+ */
+#ifndef SPEAR_H
+#define SPEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spear_status {
+  SPEAR_OK = 0,
+  SPEAR_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad shape or enum */
+  SPEAR_ERR_UNSUPPORTED = 2,      /* valid request outside what the kernels cover */
+  SPEAR_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+  SPEAR_ERR_HIP = 4               /* the HIP runtime reported an error */
+} spear_status_t;
+
+typedef enum spear_dtype { SPEAR_F16 = 0, SPEAR_BF16 = 1 } spear_dtype_t;
+
+typedef void *spear_stream_t; /* a hipStream_t */
+
+/*
+ * One compensated 4-bit layer.  All pointers are device memory.
+ *
+ *   N, K        output and input features.  K % 32 == 0 (the packed rows are
+ *               consumed in 16-byte pieces); N >= 1.
+ *   group_size  G: columns per scale/zero-point group.  G == K means one
+ *               group per output row (per-channel).  Otherwise G % 128 == 0
+ *               and K % G == 0.
+ *   qweight     int32 [N][K/8], 16-byte aligned.  Code k = 8j+i of row n is
+ *               bits 4i..4i+3 of word j of that row (lowest nibble first),
+ *               unsigned 0..15.  spear_pack_int4 produces this layout.
+ *   scales      fp16 bit patterns [N][K/G], row-major.
+ *   zeros       fp16 bit patterns [N][K/G]: the zero-point as a code value
+ *               (not pre-multiplied by the scale).
+ *   rank        r >= 0.  r == 0 is the plain 4-bit product: A, B and w_gate
+ *               are then ignored and may be NULL.  r <= SPEAR_MAX_RANK.
+ *   A           [r][K] activation type, row-major (the down-projection).
+ *   B           [N][r] activation type, row-major (the up-projection).
+ *   w_gate      [K] activation type (gate weights).
+ *   b_gate      gate bias; +INFINITY gives g == 1 and -INFINITY gives g == 0
+ *               exactly (for finite w_gate . x).
+ */
+typedef struct spear_layer {
+  int32_t N, K, group_size;
+  const int32_t *qweight;
+  const uint16_t *scales;
+  const uint16_t *zeros;
+  int32_t rank;
+  const void *A;
+  const void *B;
+  const void *w_gate;
+  float b_gate;
+} spear_layer_t;
+
+#define SPEAR_MAX_RANK 128
+#define SPEAR_MAX_DECODE_M 32
+
+/*
+ * Workspace bytes that spear_linear_decode, spear_linear_prefill and
+ * spear_linear need for this layer for any call with 1..M tokens.
+ * Returns 0 when the layer or M is invalid.  The workspace is caller-owned
+ * device memory, 256-byte aligned, and must be ZEROED ONCE before its first
+ * use; every call leaves it ready for the next one.  Calls that may run
+ * concurrently (different streams) need different workspaces.
+ */
+size_t spear_workspace_bytes(const spear_layer_t *layer, int32_t M);
+
+/*
+ * Pack 4-bit codes: q uint8 [N][K] (device; only the low 4 bits of each byte
+ * are used) -> qweight int32 [N][K/8] (device, 16-byte aligned) in the
+ * layout described at spear_layer_t.  K % 8 == 0.  Bit-exact.
+ * Not a step of the layer itself: the packing done once per layer.
+ */
+spear_status_t spear_pack_int4(const uint8_t *q, int32_t *qweight, int64_t N, int64_t K,
+                               spear_stream_t stream);
+
+/*
+ * Decode path (2.2 A, decode phase): one fused kernel for 1 <= M <= 32 tokens.
+ * x [M][K] and y [M][N] are row-major activation-type device arrays, x and y
+ * 16-byte aligned.  The gate, A x and the gated B (A x) term are computed in
+ * the same launch as the 4-bit product and added before y is rounded.
+ * M == 0 is a no-op.
+ */
+spear_status_t spear_linear_decode(const spear_layer_t *layer, spear_dtype_t dtype,
+                                   const void *x, void *y, int32_t M, void *workspace,
+                                   size_t workspace_bytes, spear_stream_t stream);
+
+/*
+ * Prefill path (2.2 A, prefill phase): any M >= 1.  The 4-bit product runs on
+ * main_stream as an MFMA GEMM over LDS-staged dequantized tiles; the
+ * compensator's thin products (gate, A x, scaled by the gate) run on
+ * aux_stream concurrently, and main_stream joins aux_stream before the
+ * gated B (A x) term is added to y.  aux_stream == NULL (or equal to
+ * main_stream) runs everything in order on main_stream.  When the call
+ * returns, work on aux_stream is ordered after main_stream's prior work and
+ * main_stream's later work is ordered after all of it.
+ */
+spear_status_t spear_linear_prefill(const spear_layer_t *layer, spear_dtype_t dtype,
+                                    const void *x, void *y, int32_t M, void *workspace,
+                                    size_t workspace_bytes, spear_stream_t main_stream,
+                                    spear_stream_t aux_stream);
+
+/*
+ * Phase-aware dispatch (2.2 A): M <= spear_get_decode_max_m() goes to the
+ * decode path on main_stream, larger M to the prefill path.
+ */
+spear_status_t spear_linear(const spear_layer_t *layer, spear_dtype_t dtype, const void *x,
+                            void *y, int32_t M, void *workspace, size_t workspace_bytes,
+                            spear_stream_t main_stream, spear_stream_t aux_stream);
+
+/* Dispatch threshold for spear_linear, 1..SPEAR_MAX_DECODE_M (default 32). Process-wide. */
+spear_status_t spear_set_decode_max_m(int32_t m);
+int32_t spear_get_decode_max_m(void);
+
+/*
+ * Chunk selector (2.2 C), host only: among n candidate prefill chunk sizes
+ * with predicted step latencies pred_ms (host arrays), return the largest
+ * chunk whose prediction is <= budget_ms (compared in float).  If none fits,
+ * return the smallest chunk and set *violated = 1 (else 0; violated may be
+ * NULL).  Returns -1 for invalid arguments (n < 1, NULL arrays, a chunk < 1).
+ */
+int32_t spear_select_chunk(const int32_t *chunks, const float *pred_ms, int32_t n,
+                           float budget_ms, int32_t *violated);
+
+/* Static description of a status code. */
+const char *spear_status_string(spear_status_t status);
+
+/* Detail of the last error reported to the calling thread ("" if none). */
+const char *spear_last_error(void);
+
+/*
+ * Sticky error word of a workspace (device pointer), copied to *flags
+ * (host) with a synchronous read on `stream`.  Bit 0 set: a decode launch
+ * gave up waiting for its compensator producers (bounded wait).  Diagnostic
+ * only; this call synchronises the stream.
+ */
+spear_status_t spear_workspace_flags(const void *workspace, uint32_t *flags,
+                                     spear_stream_t stream);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t spear_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEAR_H */

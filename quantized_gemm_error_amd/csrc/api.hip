@@ -1,0 +1,223 @@
+// C ABI of libspear: host-side validation, workspace sizing, phase-aware
+// dispatch and the chunk selector.  Every check happens before any launch;
+// on error nothing is enqueued and the outputs are untouched.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "internal.h"
+
+using namespace spear;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+std::atomic<int32_t> g_decode_max_m{SPEAR_MAX_DECODE_M};
+
+spear_status_t fail(spear_status_t st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+spear_status_t ok() {
+  g_last_error[0] = '\0';
+  return SPEAR_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validate a layer; fill the descriptor.
+spear_status_t check_layer(const spear_layer_t *layer, LayerDesc *d) {
+  if (!layer) return fail(SPEAR_ERR_INVALID_ARGUMENT, "layer is NULL");
+  const spear_layer_t &l = *layer;
+  if (l.N < 1 || l.K < 1) return fail(SPEAR_ERR_INVALID_ARGUMENT, "N=%d K=%d must be >= 1", l.N, l.K);
+  if (l.K % 8 != 0) return fail(SPEAR_ERR_INVALID_ARGUMENT, "K=%d is not a multiple of 8", l.K);
+  if (l.K % 32 != 0)
+    return fail(SPEAR_ERR_UNSUPPORTED, "K=%d: the kernels need K %% 32 == 0", l.K);
+  if (l.group_size < 1 || l.K % l.group_size != 0)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "group_size=%d must divide K=%d", l.group_size, l.K);
+  if (l.group_size != l.K && l.group_size % 128 != 0)
+    return fail(SPEAR_ERR_UNSUPPORTED, "group_size=%d: need a multiple of 128 or G == K",
+                l.group_size);
+  if (!l.qweight || !l.scales || !l.zeros)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "qweight/scales/zeros must not be NULL");
+  if (!aligned(l.qweight, 16)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "qweight not 16-byte aligned");
+  if (!aligned(l.scales, 2) || !aligned(l.zeros, 2))
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "scales/zeros not 2-byte aligned");
+  if (l.rank < 0 || l.rank > SPEAR_MAX_RANK)
+    return fail(l.rank < 0 ? SPEAR_ERR_INVALID_ARGUMENT : SPEAR_ERR_UNSUPPORTED,
+                "rank=%d outside 0..%d", l.rank, SPEAR_MAX_RANK);
+  if (l.rank > 0) {
+    if (!l.A || !l.B || !l.w_gate)
+      return fail(SPEAR_ERR_INVALID_ARGUMENT, "rank>0 needs A, B and w_gate");
+    if (!aligned(l.A, 16) || !aligned(l.w_gate, 16))
+      return fail(SPEAR_ERR_INVALID_ARGUMENT, "A and w_gate must be 16-byte aligned");
+    if (!aligned(l.B, 2)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "B not 2-byte aligned");
+    if (isnan(l.b_gate)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "b_gate is NaN");
+  }
+  d->N = l.N;
+  d->K = l.K;
+  d->G = l.group_size;
+  d->ngroups = l.K / l.group_size;
+  d->rank = l.rank;
+  d->per_channel = (l.group_size == l.K);
+  d->qw = (const uint32_t *)l.qweight;
+  d->scales = l.scales;
+  d->zeros = l.zeros;
+  d->A = (const uint16_t *)l.A;
+  d->B = (const uint16_t *)l.B;
+  d->wg = (const uint16_t *)l.w_gate;
+  d->b_gate = l.b_gate;
+  return SPEAR_OK;
+}
+
+spear_status_t check_io(spear_dtype_t dtype, const void *x, void *y) {
+  if (dtype != SPEAR_F16 && dtype != SPEAR_BF16)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "dtype=%d is not SPEAR_F16 or SPEAR_BF16", (int)dtype);
+  if (!x || !y) return fail(SPEAR_ERR_INVALID_ARGUMENT, "x and y must not be NULL");
+  if (!aligned(x, 16)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "x not 16-byte aligned");
+  if (!aligned(y, 2)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "y not 2-byte aligned");
+  if (x == y) return fail(SPEAR_ERR_INVALID_ARGUMENT, "y must not alias x");
+  return SPEAR_OK;
+}
+
+spear_status_t check_ws(void *ws, size_t have, size_t need) {
+  if (need == 0) return SPEAR_OK;
+  if (!ws) return fail(SPEAR_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (!aligned(ws, 256)) return fail(SPEAR_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (have < need)
+    return fail(SPEAR_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, have);
+  return SPEAR_OK;
+}
+
+spear_status_t hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(SPEAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spear_workspace_bytes(const spear_layer_t *layer, int32_t M) {
+  LayerDesc d;
+  if (check_layer(layer, &d) != SPEAR_OK || M < 0) return 0;
+  // enough for every call with 1..M tokens: both needs grow with M
+  size_t need = prefill_workspace_bytes(d, M < 1 ? 1 : M);
+  const size_t dec = decode_workspace_bytes(d, M < 1 ? 1 : (M < SPEAR_MAX_DECODE_M ? M : SPEAR_MAX_DECODE_M));
+  if (dec > need) need = dec;
+  return need < 256 ? 256 : need;
+}
+
+spear_status_t spear_pack_int4(const uint8_t *q, int32_t *qweight, int64_t N, int64_t K,
+                               spear_stream_t stream) {
+  if (N < 0 || K < 0) return fail(SPEAR_ERR_INVALID_ARGUMENT, "N and K must be >= 0");
+  if (K % 8 != 0) return fail(SPEAR_ERR_INVALID_ARGUMENT, "K=%lld is not a multiple of 8", (long long)K);
+  if (N == 0 || K == 0) return ok();
+  if (!q || !qweight) return fail(SPEAR_ERR_INVALID_ARGUMENT, "q and qweight must not be NULL");
+  if (!aligned(qweight, 4)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "qweight not 4-byte aligned");
+  return hip_status(launch_pack_int4(q, qweight, N, K, (hipStream_t)stream), "pack launch");
+}
+
+spear_status_t spear_linear_decode(const spear_layer_t *layer, spear_dtype_t dtype, const void *x,
+                                   void *y, int32_t M, void *workspace, size_t workspace_bytes,
+                                   spear_stream_t stream) {
+  LayerDesc d;
+  spear_status_t st = check_layer(layer, &d);
+  if (st != SPEAR_OK) return st;
+  if (M < 0 || M > SPEAR_MAX_DECODE_M)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode M=%d outside 0..%d", M, SPEAR_MAX_DECODE_M);
+  if (M == 0) return ok();
+  if ((st = check_io(dtype, x, y)) != SPEAR_OK) return st;
+  if ((st = check_ws(workspace, workspace_bytes, decode_workspace_bytes(d, M))) != SPEAR_OK)
+    return st;
+  return hip_status(launch_decode(d, (int)dtype, (const uint16_t *)x, (uint16_t *)y, M, workspace,
+                                  (hipStream_t)stream),
+                    "decode launch");
+}
+
+spear_status_t spear_linear_prefill(const spear_layer_t *layer, spear_dtype_t dtype, const void *x,
+                                    void *y, int32_t M, void *workspace, size_t workspace_bytes,
+                                    spear_stream_t main_stream, spear_stream_t aux_stream) {
+  LayerDesc d;
+  spear_status_t st = check_layer(layer, &d);
+  if (st != SPEAR_OK) return st;
+  if (M < 0) return fail(SPEAR_ERR_INVALID_ARGUMENT, "prefill M=%d must be >= 0", M);
+  if (M == 0) return ok();
+  if (M > (1 << 24)) return fail(SPEAR_ERR_UNSUPPORTED, "prefill M=%d too large", M);
+  if ((st = check_io(dtype, x, y)) != SPEAR_OK) return st;
+  if ((st = check_ws(workspace, workspace_bytes, prefill_workspace_bytes(d, M))) != SPEAR_OK)
+    return st;
+  return hip_status(launch_prefill(d, (int)dtype, (const uint16_t *)x, (uint16_t *)y, M, workspace,
+                                   (hipStream_t)main_stream, (hipStream_t)aux_stream),
+                    "prefill launch");
+}
+
+spear_status_t spear_linear(const spear_layer_t *layer, spear_dtype_t dtype, const void *x, void *y,
+                            int32_t M, void *workspace, size_t workspace_bytes,
+                            spear_stream_t main_stream, spear_stream_t aux_stream) {
+  if (M >= 0 && M <= g_decode_max_m.load())
+    return spear_linear_decode(layer, dtype, x, y, M, workspace, workspace_bytes, main_stream);
+  return spear_linear_prefill(layer, dtype, x, y, M, workspace, workspace_bytes, main_stream,
+                              aux_stream);
+}
+
+spear_status_t spear_set_decode_max_m(int32_t m) {
+  if (m < 1 || m > SPEAR_MAX_DECODE_M)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode_max_m=%d outside 1..%d", m, SPEAR_MAX_DECODE_M);
+  g_decode_max_m.store(m);
+  return ok();
+}
+
+int32_t spear_get_decode_max_m(void) { return g_decode_max_m.load(); }
+
+int32_t spear_select_chunk(const int32_t *chunks, const float *pred_ms, int32_t n, float budget_ms,
+                           int32_t *violated) {
+  if (!chunks || !pred_ms || n < 1) {
+    fail(SPEAR_ERR_INVALID_ARGUMENT, "select_chunk needs n >= 1 candidates");
+    return -1;
+  }
+  int32_t best = -1, smallest = -1;
+  for (int32_t i = 0; i < n; ++i) {
+    if (chunks[i] < 1) {
+      fail(SPEAR_ERR_INVALID_ARGUMENT, "chunk %d is %d (< 1)", i, chunks[i]);
+      return -1;
+    }
+    if (smallest < 0 || chunks[i] < smallest) smallest = chunks[i];
+    if (pred_ms[i] <= budget_ms && chunks[i] > best) best = chunks[i];
+  }
+  if (violated) *violated = best < 0 ? 1 : 0;
+  ok();
+  return best < 0 ? smallest : best;
+}
+
+const char *spear_status_string(spear_status_t status) {
+  switch (status) {
+    case SPEAR_OK: return "ok";
+    case SPEAR_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SPEAR_ERR_UNSUPPORTED: return "unsupported";
+    case SPEAR_ERR_WORKSPACE: return "workspace missing or too small";
+    case SPEAR_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *spear_last_error(void) { return g_last_error; }
+
+spear_status_t spear_workspace_flags(const void *workspace, uint32_t *flags, spear_stream_t stream) {
+  if (!workspace || !flags) return fail(SPEAR_ERR_INVALID_ARGUMENT, "workspace and flags required");
+  hipError_t e = hipMemcpyAsync(flags, (const char *)workspace + offsetof(WsHeader, flags) + offsetof(WsCounter, v),
+                                sizeof(uint32_t), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  return hip_status(e, "workspace flags read");
+}
+
+int32_t spear_version(void) { return 100; }
+
+}  // extern "C"

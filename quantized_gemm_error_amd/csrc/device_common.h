@@ -1,0 +1,124 @@
+// Device helpers for the gfx950 kernels of libspear: vector types, the
+// 4-bit dequantization into MFMA operands, MFMA wrappers, the sigmoid gate
+// and the packed-operand permutation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spear {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From &v) {
+  static_assert(sizeof(To) == sizeof(From), "bitcast size");
+  return __builtin_bit_cast(To, v);
+}
+
+// D = A * B + C for one 16x16x32 block.  Lane l supplies row (l % 16) of A
+// and column (l % 16) of B, eight K-values each from K-slot group l / 16.
+// D lands as rows 4 * (l / 16) + v, column l % 16, v = 0..3.
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  if constexpr (DT == DT_F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c,
+                                                  0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b),
+                                                   c, 0, 0, 0);
+  }
+}
+
+// fp32 16x16x4 block: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16].
+__device__ __forceinline__ f32x4_t mfma_16x16x4_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Per-row zero-point constant for dequant_word.
+//   fp16: packed pair of -(1024 + z) (exact: 1024 + z is an integer < 2048).
+//   bf16: 2^23 + z as an fp32 bit pattern.
+template <int DT>
+__device__ __forceinline__ uint32_t zero_constant(uint16_t z_f16_bits) {
+  const float z = (float)bitcast<_Float16>(z_f16_bits);
+  if constexpr (DT == DT_F16) {
+    const _Float16 nz = (_Float16)(-(1024.0f + z));
+    const uint32_t b = bitcast<uint16_t>(nz);
+    return b | (b << 16);
+  } else {
+    return bitcast<uint32_t>(8388608.0f + z);
+  }
+}
+
+// One packed word (codes q0..q7, lowest nibble first) to the exact values
+// q_i - z in the activation type, as four dwords holding the pairs
+// (q0,q4) (q1,q5) (q2,q6) (q3,q7).  The activation operand that meets these
+// in an MFMA is permuted the same way (permute_8).
+//
+// fp16: (nibble | 0x6400) read as binary16 is 1024 + q exactly; subtracting
+//       1024 + z leaves q - z exactly (an integer of magnitude <= 15).
+// bf16: (nibble | 0x4B000000) read as binary32 is 2^23 + q exactly; after
+//       subtracting 2^23 + z the integer q - z converts to bf16 exactly.
+template <int DT>
+__device__ __forceinline__ u32x4_t dequant_word(uint32_t w, uint32_t zc) {
+  u32x4_t r;
+  if constexpr (DT == DT_F16) {
+    const f16x2_t nz = bitcast<f16x2_t>(zc);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t m = ((w >> (4 * t)) & 0x000F000Fu) | 0x64006400u;
+      r[t] = bitcast<uint32_t>(bitcast<f16x2_t>(m) + nz);
+    }
+  } else {
+    const float zf = bitcast<float>(zc);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float lo = bitcast<float>(((w >> (4 * t)) & 0xFu) | 0x4B000000u) - zf;
+      const float hi = bitcast<float>(((w >> (4 * t + 16)) & 0xFu) | 0x4B000000u) - zf;
+      const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+      r[t] = bitcast<uint32_t>(p);
+    }
+  }
+  return r;
+}
+
+// Eight consecutive activation values (natural order) to the order
+// (x0,x4,x1,x5,x2,x6,x3,x7) that matches dequant_word's pairs.
+__device__ __forceinline__ u32x4_t permute_8(u32x4_t v) {
+  const u16x8_t h = bitcast<u16x8_t>(v);
+  const u16x8_t p = __builtin_shufflevector(h, h, 0, 4, 1, 5, 2, 6, 3, 7);
+  return bitcast<u32x4_t>(p);
+}
+
+template <int DT>
+__device__ __forceinline__ float to_f32(uint16_t bits) {
+  if constexpr (DT == DT_F16) {
+    return (float)bitcast<_Float16>(bits);
+  } else {
+    return bitcast<float>((uint32_t)bits << 16);
+  }
+}
+
+// Round to nearest even into the activation type.
+template <int DT>
+__device__ __forceinline__ uint16_t from_f32(float v) {
+  if constexpr (DT == DT_F16) {
+    return bitcast<uint16_t>((_Float16)v);
+  } else {
+    return bitcast<uint16_t>((__bf16)v);
+  }
+}
+
+// Logistic gate.  exp(-z) overflows to +inf for very negative z, which
+// gives exactly 0; z = +inf gives exactly 1; z = 0 gives exactly 1/2.
+__device__ __forceinline__ float gate_sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+}  // namespace spear

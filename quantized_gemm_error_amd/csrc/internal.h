@@ -1,0 +1,66 @@
+// Host-side declarations shared by the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/spear.h"
+
+namespace spear {
+
+// One counter per 128-byte line, so that atomics on different counters do
+// not queue on the same line.
+struct alignas(128) WsCounter {
+  uint32_t v;
+  uint32_t pad[31];
+};
+
+// Workspace header: the first 2048 bytes of every workspace.  Zeroed once by
+// the caller; each decode launch that uses it leaves the counters at zero.
+struct WsHeader {
+  WsCounter arrive;    // compensator producers that published their partials
+  WsCounter flags;     // sticky diagnostics (bit 0: bounded wait expired)
+  WsCounter done_top;  // slots of finished workgroups that are complete
+  WsCounter done[8];   // finished workgroups, by blockIdx % 8
+  WsCounter pad[5];
+};
+static_assert(sizeof(WsHeader) == 2048, "workspace header is 2048 bytes");
+
+constexpr int kDecodeKSplit = 4;  // K-splits of the decode compensator producers
+
+// Everything a launcher needs, already validated.
+struct LayerDesc {
+  int N, K, G, ngroups, rank;
+  bool per_channel;
+  const uint32_t *qw;
+  const uint16_t *scales, *zeros;
+  const uint16_t *A, *B, *wg;
+  float b_gate;
+};
+
+// Derived decode launch geometry.
+struct DecodePlan {
+  int mb;          // 16-token blocks (1 or 2)
+  int n_tiles;     // 16-row output tiles
+  int rb_a;        // 16-row blocks of [A; w_g]
+  int ks;          // K-splits of the producers
+  int producers;   // rb_a * ks (0 when rank == 0)
+  int nb, nbw;     // 128-wide K blocks; block iterations per wave
+  int xmode;       // 0: all of x staged once; 1: staged in chunks
+  int ci, xc;      // chunk: block iterations and K columns
+  int xstr;        // LDS row stride of the staged activation (halves)
+  size_t lds;      // dynamic LDS bytes
+};
+
+DecodePlan plan_decode(const LayerDesc &L, int M);
+size_t decode_workspace_bytes(const LayerDesc &L, int M);
+size_t prefill_workspace_bytes(const LayerDesc &L, int M);
+
+hipError_t launch_pack_int4(const uint8_t *q, int32_t *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
+                         void *ws, hipStream_t s);
+hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
+                          void *ws, hipStream_t main_s, hipStream_t aux_s);
+
+}  // namespace spear

@@ -1,0 +1,284 @@
+"""Thin ctypes binding of libspear (include/spear.h), same names as the C ABI.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libspear.so.  PyTorch supplies device memory and streams.  There is no
+fallback: if the library is missing, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspear.so")
+
+SPEAR_OK = 0
+SPEAR_ERR_INVALID_ARGUMENT = 1
+SPEAR_ERR_UNSUPPORTED = 2
+SPEAR_ERR_WORKSPACE = 3
+SPEAR_ERR_HIP = 4
+SPEAR_F16 = 0
+SPEAR_BF16 = 1
+SPEAR_MAX_RANK = 128
+SPEAR_MAX_DECODE_M = 32
+
+# Every function the header declares, for the export check.
+EXPORTED = (
+    "spear_workspace_bytes", "spear_pack_int4", "spear_linear_decode", "spear_linear_prefill",
+    "spear_linear", "spear_set_decode_max_m", "spear_get_decode_max_m", "spear_select_chunk",
+    "spear_status_string", "spear_last_error", "spear_workspace_flags", "spear_version",
+)
+
+
+class SpearError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"spear status {status}: {message}")
+        self.status = status
+
+
+class SpearLayerC(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("group_size", ctypes.c_int32),
+        ("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
+        ("rank", ctypes.c_int32),
+        ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+        ("b_gate", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libspear.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m quantized_gemm_error_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    LP = ctypes.POINTER(SpearLayerC)
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.spear_workspace_bytes.argtypes = [LP, i32]
+    lib.spear_workspace_bytes.restype = sz
+    lib.spear_pack_int4.argtypes = [P, P, i64, i64, P]
+    lib.spear_pack_int4.restype = i32
+    lib.spear_linear_decode.argtypes = [LP, i32, P, P, i32, P, sz, P]
+    lib.spear_linear_decode.restype = i32
+    lib.spear_linear_prefill.argtypes = [LP, i32, P, P, i32, P, sz, P, P]
+    lib.spear_linear_prefill.restype = i32
+    lib.spear_linear.argtypes = [LP, i32, P, P, i32, P, sz, P, P]
+    lib.spear_linear.restype = i32
+    lib.spear_set_decode_max_m.argtypes = [i32]
+    lib.spear_set_decode_max_m.restype = i32
+    lib.spear_get_decode_max_m.argtypes = []
+    lib.spear_get_decode_max_m.restype = i32
+    lib.spear_select_chunk.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float), i32,
+                                       ctypes.c_float, ctypes.POINTER(i32)]
+    lib.spear_select_chunk.restype = i32
+    lib.spear_status_string.argtypes = [i32]
+    lib.spear_status_string.restype = ctypes.c_char_p
+    lib.spear_last_error.argtypes = []
+    lib.spear_last_error.restype = ctypes.c_char_p
+    lib.spear_workspace_flags.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
+    lib.spear_workspace_flags.restype = i32
+    lib.spear_version.argtypes = []
+    lib.spear_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != SPEAR_OK:
+        lib = load_library()
+        raise SpearError(status, f"{lib.spear_status_string(status).decode()}: "
+                                 f"{lib.spear_last_error().decode()}")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return SPEAR_F16
+    if t.dtype == torch.bfloat16:
+        return SPEAR_BF16
+    raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
+
+
+@dataclass
+class SpearLayer:
+    """Device tensors of one compensated 4-bit layer (see spear_layer_t)."""
+
+    N: int
+    K: int
+    group_size: int
+    qweight: object             # int32 [N][K/8]
+    scales: object              # float16 [N][K/G]
+    zeros: object               # float16 [N][K/G]
+    rank: int = 0
+    A: object = None            # [r][K] activation dtype
+    B: object = None            # [N][r]
+    w_gate: object = None       # [K]
+    b_gate: float = 0.0
+
+    def as_c(self) -> SpearLayerC:
+        return SpearLayerC(self.N, self.K, self.group_size, _ptr(self.qweight), _ptr(self.scales),
+                           _ptr(self.zeros), self.rank, _ptr(self.A), _ptr(self.B),
+                           _ptr(self.w_gate), float(self.b_gate))
+
+    def without_compensator(self) -> "SpearLayer":
+        return SpearLayer(self.N, self.K, self.group_size, self.qweight, self.scales, self.zeros)
+
+
+def spear_workspace_bytes(layer: SpearLayer, M: int) -> int:
+    c = layer.as_c()
+    return int(load_library().spear_workspace_bytes(ctypes.byref(c), int(M)))
+
+
+def new_workspace(layer: SpearLayer, M: int, device="cuda"):
+    """A zeroed, 256-byte aligned workspace for calls on `layer` with up to M tokens."""
+    import torch
+    n = spear_workspace_bytes(layer, M)
+    if n == 0:
+        raise SpearError(SPEAR_ERR_INVALID_ARGUMENT, "invalid layer or M for a workspace")
+    buf = torch.zeros(n + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + n]
+
+
+def spear_pack_int4(q, qweight=None, stream=None):
+    """uint8 codes [N][K] (device) -> int32 packed words [N][K/8] (device)."""
+    import torch
+    N, K = q.shape
+    if qweight is None:
+        qweight = torch.empty((N, K // 8), dtype=torch.int32, device=q.device)
+    _check(load_library().spear_pack_int4(_ptr(q), _ptr(qweight), N, K, _stream(stream)))
+    return qweight
+
+
+def _io(layer, x, y):
+    import torch
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, layer.N), dtype=x.dtype, device=x.device)
+    return M, y
+
+
+def spear_linear_decode(layer: SpearLayer, x, y=None, workspace=None, stream=None):
+    M, y = _io(layer, x, y)
+    c = layer.as_c()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().spear_linear_decode(ctypes.byref(c), _dtype_code(x), _ptr(x), _ptr(y), M,
+                                              _ptr(workspace), ws_bytes, _stream(stream)))
+    return y
+
+
+def spear_linear_prefill(layer: SpearLayer, x, y=None, workspace=None, main_stream=None,
+                         aux_stream=None):
+    M, y = _io(layer, x, y)
+    c = layer.as_c()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    aux = None if aux_stream is None else _stream(aux_stream)
+    _check(load_library().spear_linear_prefill(ctypes.byref(c), _dtype_code(x), _ptr(x), _ptr(y), M,
+                                               _ptr(workspace), ws_bytes, _stream(main_stream), aux))
+    return y
+
+
+def spear_linear(layer: SpearLayer, x, y=None, workspace=None, main_stream=None, aux_stream=None):
+    M, y = _io(layer, x, y)
+    c = layer.as_c()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    aux = None if aux_stream is None else _stream(aux_stream)
+    _check(load_library().spear_linear(ctypes.byref(c), _dtype_code(x), _ptr(x), _ptr(y), M,
+                                       _ptr(workspace), ws_bytes, _stream(main_stream), aux))
+    return y
+
+
+def spear_set_decode_max_m(m: int) -> None:
+    _check(load_library().spear_set_decode_max_m(int(m)))
+
+
+def spear_get_decode_max_m() -> int:
+    return int(load_library().spear_get_decode_max_m())
+
+
+def spear_select_chunk(chunks, pred_ms, budget_ms: float):
+    """Largest chunk whose predicted latency fits the budget -> (chunk, violated)."""
+    n = len(chunks)
+    if n != len(pred_ms):
+        raise ValueError("chunks and pred_ms differ in length")
+    ca = (ctypes.c_int32 * max(n, 1))(*[int(c) for c in chunks])
+    pa = (ctypes.c_float * max(n, 1))(*[float(p) for p in pred_ms])
+    viol = ctypes.c_int32(0)
+    lib = load_library()
+    c = lib.spear_select_chunk(ca, pa, n, ctypes.c_float(budget_ms), ctypes.byref(viol))
+    if c < 0:
+        raise SpearError(SPEAR_ERR_INVALID_ARGUMENT, lib.spear_last_error().decode())
+    return int(c), bool(viol.value)
+
+
+def spear_status_string(status: int) -> str:
+    return load_library().spear_status_string(int(status)).decode()
+
+
+def spear_last_error() -> str:
+    return load_library().spear_last_error().decode()
+
+
+def spear_workspace_flags(workspace, stream=None) -> int:
+    flags = ctypes.c_uint32(0)
+    _check(load_library().spear_workspace_flags(_ptr(workspace), ctypes.byref(flags), _stream(stream)))
+    return int(flags.value)
+
+
+def spear_version() -> int:
+    return int(load_library().spear_version())
+
+
+def layer_to_device(host_layer, device="cuda", stream=None) -> SpearLayer:
+    """Upload a synth.SynthLayer (unpacked codes) and pack it on the GPU."""
+    import numpy as np
+    import torch
+    act = torch.float16 if host_layer.dtype == "f16" else torch.bfloat16
+
+    def up(arr, dt):
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device)
+        return t.view(dt)
+
+    q = torch.from_numpy(np.ascontiguousarray(host_layer.q)).to(device)
+    qweight = spear_pack_int4(q, stream=stream)
+    lay = SpearLayer(N=host_layer.N, K=host_layer.K, group_size=host_layer.group_size,
+                     qweight=qweight, scales=up(host_layer.scales, torch.float16),
+                     zeros=up(host_layer.zeros, torch.float16), rank=host_layer.rank,
+                     b_gate=host_layer.b_gate)
+    if host_layer.rank > 0:
+        lay.A = up(host_layer.A, act)
+        lay.B = up(host_layer.B, act)
+        lay.w_gate = up(host_layer.w_gate, act)
+    return lay
+
+
+def act_to_device(bits, dtype: str, device="cuda"):
+    """uint16 activation bit patterns (numpy) -> float16/bfloat16 device tensor."""
+    import numpy as np
+    import torch
+    act = torch.float16 if dtype == "f16" else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(act)
+
+
+def inf_gate(sign: int) -> float:
+    return math.copysign(math.inf, sign)

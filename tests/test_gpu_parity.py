@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bar: packing bit-exact; outputs |y - y_ref| <= 1e-2 (1 + |y_ref|) elementwise
+(fp16/bf16 output, fp32 arithmetic); the gate-off layer bit-identical to the
+rank-0 layer.  Small shapes are compared in full (several tiles plus ragged
+tails in N, M and K); the Llama-shaped layers on sampled output rows.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_gemm_error_amd import spear, synth
+
+from gpu_helpers import assert_close, gpu_y_f64, note, oracle_y, run, sample_rows, to_host_bits
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+DEV = "cuda"
+
+
+def _setup(N, K, G, r, seed, dtype="f16", M=1, outliers=False, **kw):
+    hl = synth.make_layer(N, K, G, r, seed=seed, dtype=dtype, **kw)
+    x_bits = synth.make_activations(M, K, seed=seed, dtype=dtype, outliers=outliers)
+    lay = spear.layer_to_device(hl, DEV)
+    x = spear.act_to_device(x_bits, dtype, DEV)
+    return hl, x_bits, lay, x
+
+
+def _ws_header(ws):
+    """Workspace counters (arrive, flags, done_top, done[0..7]); one per 128-byte line."""
+    words = ws[:2048].view(torch.int32).cpu().tolist()
+    return [words[32 * i] for i in range(11)]
+
+
+# ---------------------------------------------------------------------------
+# packing
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("N,K", [(1, 8), (3, 24), (64, 256), (37, 4104), (512, 4096)])
+def test_pack_bit_exact(N, K):
+    note(f"pack N={N} K={K}")
+    rng = np.random.default_rng(N * 7 + K)
+    q = rng.integers(0, 256, size=(N, K), dtype=np.uint8)  # high bits must be ignored
+    qd = torch.from_numpy(q).to(DEV)
+    words = spear.spear_pack_int4(qd)
+    torch.cuda.synchronize()
+    assert np.array_equal(words.cpu().numpy(), oracle.pack_int4(q))
+
+
+# ---------------------------------------------------------------------------
+# worked example (hand-derived values, exact in fp16)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_hand_example_exact(path, golden_dir):
+    note(f"hand example {path}")
+    ex = json.load(open(os.path.join(golden_dir, "hand_example.json")))
+    K = 32  # the 8-column example embedded in K = 32 with zero padding
+    q = np.zeros((2, K), np.uint8)
+    q[:, :8] = np.array(ex["codes"], np.uint8)
+    s = synth.to_f16_bits(np.array(ex["scales"], np.float32)[:, None])
+    z = synth.to_f16_bits(np.array(ex["zeros"], np.float32)[:, None])
+    xv = np.zeros((1, K), np.float32)
+    xv[0, :8] = ex["x"]
+    Av = np.zeros((1, K), np.float32)
+    Av[0, :8] = ex["A"][0]
+    wgv = np.zeros(K, np.float32)
+    wgv[:8] = ex["w_gate"]
+    for case in ex["cases"]:
+        hl = synth.SynthLayer(N=2, K=K, group_size=K, rank=1, dtype="f16", q=q, scales=s, zeros=z,
+                              A=synth.to_f16_bits(Av), B=synth.to_f16_bits(np.array(ex["B"], np.float32)),
+                              w_gate=synth.to_f16_bits(wgv), b_gate=float(case["b_gate"]))
+        lay = spear.layer_to_device(hl, DEV)
+        x = spear.act_to_device(synth.to_f16_bits(xv), "f16", DEV)
+        ws = spear.new_workspace(lay, 1)
+        y = run(path, lay, x, ws)
+        torch.cuda.synchronize()
+        assert gpu_y_f64(y, "f16")[0].tolist() == case["y"], case
+
+
+# ---------------------------------------------------------------------------
+# decode parity, full outputs
+# ---------------------------------------------------------------------------
+
+DECODE_CASES = [
+    # N, K, G, r, M, dtype, outliers
+    (512, 512, 0, 16, 1, "f16", False),      # small 512x512 per-channel, r = 16
+    (100, 256, 128, 8, 3, "f16", True),      # ragged N tile
+    (272, 544, 0, 32, 5, "f16", False),      # K not a multiple of 128 (per-channel)
+    (96, 1024, 256, 20, 16, "f16", True),    # G = 256, r not a multiple of 16
+    (130, 640, 128, 32, 17, "f16", True),    # two token blocks, ragged
+    (64, 2048, 128, 64, 32, "f16", True),    # M = 32, xc chunking
+    (200, 768, 128, 16, 7, "bf16", True),    # bf16
+    (48, 8192, 0, 4, 2, "bf16", False),      # long K, several staged chunks at M = 2
+    (33, 96, 0, 1, 1, "f16", False),         # rank 1, tiny K
+]
+
+
+@pytest.mark.parametrize("N,K,G,r,M,dtype,outl", DECODE_CASES)
+def test_decode_parity(N, K, G, r, M, dtype, outl):
+    note(f"decode N={N} K={K} G={G} r={r} M={M} {dtype}")
+    hl, xb, lay, x = _setup(N, K, G, r, seed=N + K + r + M, dtype=dtype, M=M, outliers=outl,
+                            b_gate=0.25)
+    ws = spear.new_workspace(lay, M)
+    y = spear.spear_linear_decode(lay, x, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(gpu_y_f64(y, dtype), oracle_y(hl, xb), f"decode {N}x{K} M={M}")
+    assert _ws_header(ws) == [0] * 11
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 32])
+def test_decode_gate_off_is_rank_zero_bitwise(M):
+    note(f"gate off M={M}")
+    hl, xb, lay, x = _setup(160, 1024, 128, 32, seed=5, M=M, outliers=True)
+    lay.w_gate = torch.zeros_like(lay.w_gate)
+    lay.b_gate = float("-inf")
+    ws = spear.new_workspace(lay, M)
+    y_off = spear.spear_linear_decode(lay, x, workspace=ws)
+    y_r0 = spear.spear_linear_decode(lay.without_compensator(), x)
+    torch.cuda.synchronize()
+    assert torch.equal(y_off.view(torch.int16), y_r0.view(torch.int16))
+    assert_close(gpu_y_f64(y_r0, "f16"), oracle_y(hl, xb, with_ec=False), "rank 0")
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_compensator_isolated(path):
+    """q == z makes dequant(W_q) = 0: y is the gated compensator alone."""
+    note(f"isolation {path}")
+    N, K, r, M = 144, 512, 32, 9 if path == "decode" else 70
+    rng = np.random.default_rng(3)
+    zc = rng.integers(0, 16, size=(N, K // 128))
+    q = np.repeat(zc, 128, axis=1).astype(np.uint8)
+    sK = 1.0 / np.sqrt(K)
+    hl = synth.SynthLayer(
+        N=N, K=K, group_size=128, rank=r, dtype="f16", q=q,
+        scales=synth.to_f16_bits(rng.uniform(0.005, 0.02, (N, K // 128)).astype(np.float32)),
+        zeros=synth.to_f16_bits(zc.astype(np.float32)),
+        A=synth.to_f16_bits(rng.standard_normal((r, K)).astype(np.float32) * sK),
+        B=synth.to_f16_bits(rng.standard_normal((N, r)).astype(np.float32)),
+        w_gate=synth.to_f16_bits(rng.standard_normal(K).astype(np.float32) * sK),
+        b_gate=0.1)
+    xb = synth.make_activations(M, K, seed=4)
+    lay = spear.layer_to_device(hl, DEV)
+    x = spear.act_to_device(xb, "f16", DEV)
+    ws = spear.new_workspace(lay, M)
+    y = run(path, lay, x, ws)
+    torch.cuda.synchronize()
+    ref = oracle_y(hl, xb)
+    assert np.max(np.abs(ref)) > 1.0  # the compensator term is large here
+    assert_close(gpu_y_f64(y, "f16"), ref, f"isolation {path}")
+    # and the gate is not saturated: a mix of gate values
+    x64 = oracle.f16_bits_to_f64(xb)
+    g = oracle.gate(x64, oracle.f16_bits_to_f64(hl.w_gate), hl.b_gate)
+    assert g.min() < 0.45 and g.max() > 0.55
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_full_rank_absorption(path):
+    """g = 1, A = I, B = fp16(W - dequant(W_q)): recovers the fp16 product."""
+    note(f"full rank {path}")
+    N = K = 64
+    M = 4 if path == "decode" else 40
+    hl = synth.make_layer(N, K, 0, 0, seed=21, keep_fp32=True)
+    W16 = hl.w_fp32.astype(np.float16).astype(np.float64)
+    Wq = oracle.dequant(oracle.pack_int4(hl.q), hl.scales, hl.zeros, K)
+    hl.rank = K
+    hl.A = synth.to_f16_bits(np.eye(K, dtype=np.float32))
+    hl.B = synth.to_f16_bits(W16 - Wq)
+    hl.w_gate = np.zeros(K, np.uint16)
+    hl.b_gate = float("inf")
+    xb = synth.make_activations(M, K, seed=22)
+    lay = spear.layer_to_device(hl, DEV)
+    x = spear.act_to_device(xb, "f16", DEV)
+    ws = spear.new_workspace(lay, M)
+    y = gpu_y_f64(run(path, lay, x, ws), "f16")
+    torch.cuda.synchronize()
+    assert_close(y, oracle_y(hl, xb), f"full rank {path}")
+    target = oracle.f16_bits_to_f64(xb) @ W16.T
+    assert np.max(np.abs(y - target)) < 0.05 * np.max(np.abs(target))
+
+
+def test_decode_token_independence():
+    note("token independence")
+    hl, xb, lay, x = _setup(96, 1024, 128, 16, seed=8, M=4, outliers=True)
+    ws = spear.new_workspace(lay, 4)
+    y4 = gpu_y_f64(spear.spear_linear_decode(lay, x, workspace=ws), "f16")
+    perm = [2, 0, 3, 1]
+    yp = gpu_y_f64(spear.spear_linear_decode(lay, x[perm].contiguous(), workspace=ws), "f16")
+    ones = [gpu_y_f64(spear.spear_linear_decode(lay, x[m:m + 1].contiguous(), workspace=ws), "f16")
+            for m in range(4)]
+    torch.cuda.synchronize()
+    ref = oracle_y(hl, xb)
+    assert_close(yp, ref[perm], "permuted")
+    for m in range(4):
+        assert_close(ones[m], ref[m:m + 1], f"single token {m}")
+
+
+def test_decode_workspace_reuse_many_calls():
+    note("workspace reuse")
+    hl, xb, lay, x = _setup(320, 1024, 128, 32, seed=9, M=32, outliers=True)
+    ws = spear.new_workspace(lay, 32)
+    ref = oracle_y(hl, xb)
+    outs = {}
+    for it in range(60):
+        M = [1, 32, 4, 16, 7][it % 5]
+        outs[(it, M)] = spear.spear_linear_decode(lay, x[:M].contiguous(), workspace=ws)
+    torch.cuda.synchronize()
+    for (it, M), y in outs.items():
+        assert_close(gpu_y_f64(y, "f16"), ref[:M], f"call {it} M={M}")
+    assert spear.spear_workspace_flags(ws) == 0
+    assert _ws_header(ws) == [0] * 11
+
+
+# ---------------------------------------------------------------------------
+# prefill parity
+# ---------------------------------------------------------------------------
+
+PREFILL_CASES = [
+    # N, K, G, r, M, dtype, outliers, aux
+    (512, 512, 0, 16, 64, "f16", False, True),     # small 512x512 per-channel at M = 64
+    (300, 1024, 128, 32, 200, "f16", True, True),  # ragged N and M tiles
+    (256, 640, 0, 24, 130, "bf16", True, False),   # K % 128 != 0, bf16, serial
+    (384, 768, 256, 32, 257, "bf16", True, True),  # G = 256, bf16
+    (128, 256, 128, 0, 100, "f16", False, True),   # rank 0
+    (64, 128, 128, 4, 33, "f16", False, True),     # M just above the decode range
+]
+
+
+@pytest.mark.parametrize("N,K,G,r,M,dtype,outl,aux", PREFILL_CASES)
+def test_prefill_parity(N, K, G, r, M, dtype, outl, aux):
+    note(f"prefill N={N} K={K} G={G} r={r} M={M} {dtype} aux={aux}")
+    hl, xb, lay, x = _setup(N, K, G, r, seed=N + K + r + M, dtype=dtype, M=M, outliers=outl,
+                            b_gate=-0.3)
+    ws = spear.new_workspace(lay, M)
+    stream = torch.cuda.Stream() if aux else None
+    y = spear.spear_linear_prefill(lay, x, workspace=ws, aux_stream=stream)
+    torch.cuda.synchronize()
+    assert_close(gpu_y_f64(y, dtype), oracle_y(hl, xb), f"prefill {N}x{K} M={M}")
+
+
+def test_prefill_gate_off_matches_rank_zero():
+    note("prefill gate off")
+    hl, xb, lay, x = _setup(256, 512, 128, 32, seed=11, M=96)
+    lay.w_gate = torch.zeros_like(lay.w_gate)
+    lay.b_gate = float("-inf")
+    ws = spear.new_workspace(lay, 96)
+    y_off = spear.spear_linear_prefill(lay, x, workspace=ws, aux_stream=torch.cuda.Stream())
+    y_r0 = spear.spear_linear_prefill(lay.without_compensator(), x)
+    torch.cuda.synchronize()
+    assert torch.equal(y_off.view(torch.int16), y_r0.view(torch.int16))
+
+
+def test_decode_and_prefill_agree_and_dispatch():
+    note("dispatch")
+    hl, xb, lay, x = _setup(200, 1024, 128, 32, seed=12, M=48, outliers=True)
+    ws = spear.new_workspace(lay, 48)
+    ref = oracle_y(hl, xb)
+    x32 = x[:32].contiguous()
+    yd = spear.spear_linear_decode(lay, x32, workspace=ws)
+    yp = spear.spear_linear_prefill(lay, x32, workspace=ws)
+    yl32 = spear.spear_linear(lay, x32, workspace=ws)
+    yl48 = spear.spear_linear(lay, x, workspace=ws)
+    yp48 = spear.spear_linear_prefill(lay, x, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(gpu_y_f64(yd, "f16"), ref[:32], "decode")
+    assert_close(gpu_y_f64(yp, "f16"), ref[:32], "prefill")
+    assert torch.equal(yl32.view(torch.int16), yd.view(torch.int16))     # M = 32 -> decode
+    assert torch.equal(yl48.view(torch.int16), yp48.view(torch.int16))   # M = 48 -> prefill
+
+
+# ---------------------------------------------------------------------------
+# Llama-shaped layers at full size, sampled rows
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("K,N", synth.LLAMA7B_SHAPES)
+def test_llama7b_decode_sampled(K, N):
+    w = synth.WORKLOADS["llama7b-decode"]
+    hl = synth.make_layer(N, K, w["group_size"], w["rank"], seed=w["seed"], dtype="f16")
+    lay = spear.layer_to_device(hl, DEV)
+    rows = sample_rows(N, 192, seed=K + N)
+    for M in w["tokens"]:
+        note(f"llama7b decode K={K} N={N} M={M}")
+        xb = synth.make_activations(M, K, seed=w["seed"] + M, outliers=True)
+        x = spear.act_to_device(xb, "f16", DEV)
+        ws = spear.new_workspace(lay, M)
+        y = spear.spear_linear_decode(lay, x, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(gpu_y_f64(y, "f16")[:, rows], oracle_y(hl, xb, rows=rows), f"7B {K}->{N} M={M}")
+
+
+@pytest.mark.parametrize("K,N", synth.LLAMA7B_SHAPES)
+def test_llama7b_prefill_sampled(K, N):
+    w = synth.WORKLOADS["llama7b-prefill"]
+    M = w["tokens"][0]
+    note(f"llama7b prefill K={K} N={N} M={M}")
+    hl = synth.make_layer(N, K, w["group_size"], w["rank"], seed=w["seed"], dtype="bf16")
+    xb = synth.make_activations(M, K, seed=w["seed"], dtype="bf16", outliers=True)
+    lay = spear.layer_to_device(hl, DEV)
+    x = spear.act_to_device(xb, "bf16", DEV)
+    ws = spear.new_workspace(lay, M)
+    y = spear.spear_linear_prefill(lay, x, workspace=ws, aux_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    rows = sample_rows(N, 96, seed=K)
+    toks = np.unique(np.r_[np.random.default_rng(N).choice(M, 48, replace=False), M - 1])
+    ref = oracle_y(hl, xb[toks], rows=rows)
+    assert_close(gpu_y_f64(y, "bf16")[np.ix_(toks, rows)], ref, f"7B prefill {K}->{N}")
+
+
+def test_llama70b_layer_sampled():
+    w = synth.WORKLOADS["llama70b-layer"]
+    K, N = 8192, 28672
+    hl = synth.make_layer(N, K, w["group_size"], w["rank"], seed=w["seed"], dtype="f16")
+    lay = spear.layer_to_device(hl, DEV)
+    rows = sample_rows(N, 96, seed=70)
+    for M in w["tokens"]:
+        note(f"llama70b K={K} N={N} M={M}")
+        xb = synth.make_activations(M, K, seed=w["seed"] + M)
+        x = spear.act_to_device(xb, "f16", DEV)
+        ws = spear.new_workspace(lay, M)
+        y = spear.spear_linear(lay, x, workspace=ws, aux_stream=torch.cuda.Stream())
+        torch.cuda.synchronize()
+        assert_close(gpu_y_f64(y, "f16")[:, rows], oracle_y(hl, xb, rows=rows), f"70B M={M}")
