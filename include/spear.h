@@ -67,14 +67,15 @@ typedef void *spear_stream_t; /* a hipStream_t */
  * One compensated 4-bit layer.  All pointers are device memory.
  *
  *   N, K        output and input features.  K % 32 == 0 (the packed rows are
- *               consumed in 16-byte pieces); N >= 1.
+ *               consumed in 16-byte pieces), K <= SPEAR_MAX_K; N >= 1.
  *   group_size  G: columns per scale/zero-point group.  G == K means one
  *               group per output row (per-channel).  Otherwise G % 128 == 0
  *               and K % G == 0.
  *   qweight     int32 [N][K/8], 16-byte aligned.  Code k = 8j+i of row n is
  *               bits 4i..4i+3 of word j of that row (lowest nibble first),
  *               unsigned 0..15.  spear_pack_int4 produces this layout.
- *   scales      fp16 bit patterns [N][K/G], row-major.
+ *   scales      fp16 bit patterns [N][K/G], row-major (16-byte alignment is
+ *               not required, but it is the fast path).
  *   zeros       fp16 bit patterns [N][K/G]: the zero-point as a code value
  *               (not pre-multiplied by the scale).
  *   rank        r >= 0.  r == 0 is the plain 4-bit product: A, B and w_gate
@@ -98,6 +99,7 @@ typedef struct spear_layer {
 } spear_layer_t;
 
 #define SPEAR_MAX_RANK 128
+#define SPEAR_MAX_K 131072
 #define SPEAR_MAX_DECODE_M 32
 
 /*

@@ -40,6 +40,7 @@ spear_status_t check_layer(const spear_layer_t *layer, LayerDesc *d) {
   if (l.K % 8 != 0) return fail(SPEAR_ERR_INVALID_ARGUMENT, "K=%d is not a multiple of 8", l.K);
   if (l.K % 32 != 0)
     return fail(SPEAR_ERR_UNSUPPORTED, "K=%d: the kernels need K %% 32 == 0", l.K);
+  if (l.K > SPEAR_MAX_K) return fail(SPEAR_ERR_UNSUPPORTED, "K=%d above %d", l.K, SPEAR_MAX_K);
   if (l.group_size < 1 || l.K % l.group_size != 0)
     return fail(SPEAR_ERR_INVALID_ARGUMENT, "group_size=%d must divide K=%d", l.group_size, l.K);
   if (l.group_size != l.K && l.group_size % 128 != 0)
@@ -135,6 +136,8 @@ spear_status_t spear_linear_decode(const spear_layer_t *layer, spear_dtype_t dty
     return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode M=%d outside 0..%d", M, SPEAR_MAX_DECODE_M);
   if (M == 0) return ok();
   if ((st = check_io(dtype, x, y)) != SPEAR_OK) return st;
+  if (!decode_supported(d, M))
+    return fail(SPEAR_ERR_UNSUPPORTED, "no decode launch shape fits K=%d G=%d M=%d", d.K, d.G, M);
   if ((st = check_ws(workspace, workspace_bytes, decode_workspace_bytes(d, M))) != SPEAR_OK)
     return st;
   return hip_status(launch_decode(d, (int)dtype, (const uint16_t *)x, (uint16_t *)y, M, workspace,

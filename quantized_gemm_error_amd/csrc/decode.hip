@@ -30,6 +30,7 @@
 // to finish (counted over eight slots, then across the slots) resets the
 // workspace counters for the next call.
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -40,12 +41,12 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kDepth = 8;                  // K blocks in flight per wave
+constexpr int kDepth = 4;                  // K blocks in flight per wave (one straight-line group)
 constexpr int kKS = kDecodeKSplit;         // producer K-splits
-constexpr int kMaxStepsPerWave = (SPEAR_MAX_RANK / 4 + kWaves - 1) / kWaves;  // rank steps of 4
 constexpr uint32_t kSpinLimit = 1u << 20;  // bounded wait for the producers
-constexpr int kWholeLdsBytes = 100 * 1024; // whole-x staging budget
+constexpr int kWholeLdsBytes = 132 * 1024; // whole-x staging budget
 constexpr int kChunkLdsBytes = 68 * 1024;  // chunked staging budget
+constexpr int kMaxLds = 160 * 1024;  // dynamic LDS cap (x, scale table, reduction)
 
 enum { XWHOLE = 0, XCHUNK = 1 };
 
@@ -61,6 +62,11 @@ struct DecodeArgs {
   int nb, nbw;     // 128-wide K blocks; block iterations per wave
   int ci, xc;      // chunked staging: iterations and K elements per chunk
   int xstr;        // LDS row stride of the staged activation (halves)
+  int xzero;       // column of the 128-wide zero strip in each staged row
+  int nbw_pad;     // block iterations rounded up to a multiple of kDepth
+  int sz_off;      // byte offset of the scale/zero table in dynamic LDS
+  int gmul;        // ceil(2^20 / (G / 128)): kb * gmul >> 20 == kb / (G / 128)
+  int red_off;     // byte offset of the wave-reduction buffer in dynamic LDS
   WsHeader *hdr;
   float *part;     // [producers][16 rows of A'][16 * MB tokens]
 };
@@ -71,7 +77,7 @@ __device__ __forceinline__ f32x4_t reduce_waves(f32x4_t own, f32x4_t (*red)[MB][
                                                 int lane) {
   f32x4_t v = own;
 #pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w) v = v + red[w][mb][lane];
+  for (int w = 1; w < kWaves; ++w) v = v + red[w][mb][lane];
   return v;
 }
 
@@ -128,7 +134,7 @@ __device__ void produce(const DecodeArgs &a, int p, f32x4_t (*red)[MB][64], int 
 
   if (wave > 0) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) red[wave - 1][mb][lane] = acc[mb];
+    for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
   }
   __syncthreads();
   if (wave == 0) {
@@ -181,10 +187,21 @@ __device__ __forceinline__ void whole_load(const DecodeArgs &a, XBatch &xb, int 
   const int total = a.M * per_row;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int p = min(p0 + tid + kThreads * i, total - 1);
-    const int m = p / per_row, j = p - m * per_row;
-    const int k = min(8 * j, a.K - 8);
-    xb.v[i] = *(const u32x4_t *)(a.x + (size_t)m * a.K + k);
+    if (p0 + kThreads * i < total) {  // uniform across the workgroup
+      const int p = min(p0 + tid + kThreads * i, total - 1);
+      const int m = p / per_row, j = p - m * per_row;
+      const int k = min(8 * j, a.K - 8);
+      xb.v[i] = *(const u32x4_t *)(a.x + (size_t)m * a.K + k);
+    }
+  }
+}
+
+// Zeros in columns [xzero, xzero + 128) of every staged row: blocks past the
+// end of K read them, so they add exact zeros.
+__device__ __forceinline__ void zero_strip(const DecodeArgs &a, uint16_t *xs, int tid) {
+  for (int p = tid; p < a.M * 16; p += kThreads) {
+    const int m = p / 16, j = p % 16;
+    *(u32x4_t *)(xs + m * a.xstr + a.xzero + 8 * j) = u32x4_t{0u, 0u, 0u, 0u};
   }
 }
 
@@ -195,7 +212,7 @@ __device__ __forceinline__ void whole_store(const DecodeArgs &a, const XBatch &x
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int p = p0 + tid + kThreads * i;
-    if (p < total) {
+    if (p0 + kThreads * i < total && p < total) {
       const int m = p / per_row, j = p - m * per_row;
       const u32x4_t val = (8 * j < a.K) ? xb.v[i] : u32x4_t{0u, 0u, 0u, 0u};
       *(u32x4_t *)(xs + m * a.xstr + 8 * j) = permute_8(val);
@@ -203,16 +220,54 @@ __device__ __forceinline__ void whole_store(const DecodeArgs &a, const XBatch &x
   }
 }
 
+// The tile's scales and zero-points as two LDS words per (row, group): the
+// dequant_word zero constant and the scale as fp32.  The tile's rows are
+// consecutive, so their groups form one contiguous range of rows * ngroups
+// elements in each array.
+template <int DT>
+__device__ void stage_sz(const DecodeArgs &a, int n0, int rows, uint32_t *szs, int tid) {
+  const int ng = a.ngroups;
+  const size_t base = (size_t)n0 * ng;
+  const size_t end = (size_t)a.N * ng;
+  const int cnt = rows * ng;
+  for (int p = tid; 8 * p < cnt; p += kThreads) {
+    const size_t e0 = base + 8 * (size_t)p;
+    u16x8_t sv = {0, 0, 0, 0, 0, 0, 0, 0}, zv = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (e0 + 8 <= end && ((uintptr_t)(a.scales + e0) % 16) == 0 &&
+        ((uintptr_t)(a.zeros + e0) % 16) == 0) {
+      sv = *(const u16x8_t *)(a.scales + e0);
+      zv = *(const u16x8_t *)(a.zeros + e0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (e0 + i < end) {
+          sv[i] = a.scales[e0 + i];
+          zv[i] = a.zeros[e0 + i];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (8 * p + i < cnt) {
+        szs[2 * (8 * p + i)] = zero_constant<DT>(zv[i]);
+        szs[2 * (8 * p + i) + 1] = bitcast<uint32_t>((float)bitcast<_Float16>(sv[i]));
+      }
+    }
+  }
+}
+
+constexpr int kChunkPieces = 4;  // staged 16-byte pieces per thread per chunk
+
 struct XChunk {
-  u32x4_t v[8];
+  u32x4_t v[kChunkPieces];
 };
 
-// One chunk (xc columns) of x into registers: at most 8 pieces per thread.
+// One chunk (xc columns) of x into registers: at most kChunkPieces per thread.
 __device__ __forceinline__ void chunk_load(const DecodeArgs &a, XChunk &c, int chunk, int tid) {
   const int per_row = a.xc / 8;
   const int k0 = chunk * a.xc;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kChunkPieces; ++i) {
     const int p = tid + kThreads * i;
     const int m = min(p / per_row, a.M - 1);
     const int j = p % per_row;
@@ -226,7 +281,7 @@ __device__ __forceinline__ void chunk_store(const DecodeArgs &a, const XChunk &c
   const int per_row = a.xc / 8;
   const int k0 = chunk * a.xc;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kChunkPieces; ++i) {
     const int p = tid + kThreads * i;
     const int m = p / per_row, j = p % per_row;
     if (m < a.M) {
@@ -237,44 +292,41 @@ __device__ __forceinline__ void chunk_store(const DecodeArgs &a, const XChunk &c
 }
 
 // ---------------------------------------------------------------------------
-// Consumers: 16 output rows, full K, four waves.
+// Consumers: 16 * WR output rows, full K.  The eight waves form WR row-blocks
+// of KG = 8 / WR waves; the KG waves of a row-block take interleaved K blocks
+// and all waves share the staged activation.
 // ---------------------------------------------------------------------------
-template <int DT, int MB, bool EC, bool PERCH, int XMODE>
+template <int DT, int MB, bool EC, bool PERCH, int XMODE, int WR>
 __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*red)[MB][64],
                         int tid) {
-  const int wave = tid >> 6, lane = tid & 63, col = lane & 15, h = lane >> 4;
-  const int n = tile * 16 + col;
+  constexpr int KG = kWaves / WR;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar indices
+  const int lane = tid & 63, col = lane & 15, h = lane >> 4;
+  const int wr = wave / KG, wk = wave % KG;
+  const int n0 = tile * 16 * WR;
+  const int n = n0 + 16 * wr + col;
   const int row = min(n, a.N - 1);
   const uint32_t *wrow = a.qw + (size_t)row * (a.K / 8);
-  const uint16_t *srow = a.scales + (size_t)row * a.ngroups;
-  const uint16_t *zrow = a.zeros + (size_t)row * a.ngroups;
   const int nb = a.nb, nbw = a.nbw;
 
   uint32_t zc_row = 0;
   float s_row = 0.f;
   if constexpr (PERCH) {
-    zc_row = zero_constant<DT>(zrow[0]);
-    s_row = (float)bitcast<_Float16>(srow[0]);
+    zc_row = zero_constant<DT>(a.zeros[row]);
+    s_row = (float)bitcast<_Float16>(a.scales[row]);
   }
 
-  // piece of block iteration b: block kb = kWaves b + wave (clamped), words [4h, 4h + 4)
-  u32x4_t wr[kDepth];
-  uint16_t sr[kDepth], zr[kDepth];
-  auto wload = [&](int b, u32x4_t &w, uint16_t &sv, uint16_t &zv) {
-    const int kb = min(b * kWaves + wave, nb - 1);
+  // piece of block iteration b: block kb = KG b + wk (clamped), words [4h, 4h + 4)
+  u32x4_t wr_ring[kDepth];
+  auto wload = [&](int b, u32x4_t &w) {
+    const int kb = min(b * KG + wk, nb - 1);
     const int off = (kb * 128 + 32 * h < a.K) ? kb * 16 + 4 * h : 0;
     w = *(const u32x4_t *)(wrow + off);
-    if constexpr (!PERCH) {
-      const int g = (kb * 128) / a.G;
-      sv = srow[g];
-      zv = zrow[g];
-    } else {
-      sv = 0;
-      zv = 0;
-    }
   };
+
   // activation loads first, then the weight ring, so that storing the
   // activation to LDS waits only for its own loads
+  uint32_t *szs = (uint32_t *)((char *)xs + a.sz_off);
   XChunk xc;
   XBatch xb;
   if constexpr (XMODE == XWHOLE) {
@@ -283,7 +335,9 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
     chunk_load(a, xc, 0, tid);
   }
 #pragma unroll
-  for (int i = 0; i < kDepth; ++i) wload(i, wr[i], sr[i], zr[i]);
+  for (int i = 0; i < kDepth; ++i) wload(i, wr_ring[i]);
+  if constexpr (!PERCH) stage_sz<DT>(a, n0, 16 * WR, szs, tid);
+  zero_strip(a, xs, tid);
   if constexpr (XMODE == XWHOLE) {
     whole_store(a, xb, xs, 0, tid);
     const int total = a.M * a.nb * 16;
@@ -291,14 +345,25 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
       whole_load(a, xb, p0, tid);
       whole_store(a, xb, xs, p0, tid);
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   f32x4_t acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int szrow = 2 * (16 * wr + col) * a.ngroups;
+  // A-operand rows past M read row M - 1: MFMA output rows depend only on
+  // their own A rows, and rows >= M are never stored
+  int xrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) xrow[mb] = min(col + 16 * mb, a.M - 1) * a.xstr;
 
-  for (int b0 = 0; b0 < nbw; b0 += kDepth) {
+  // groups of kDepth blocks per wave, straight-line: blocks past the end of K
+  // read the zero strip and clamped weights.  Every group but the last refills
+  // the ring; the two kinds are separate compile-time copies, so a group has
+  // no branch and its loads, LDS reads and MFMAs can interleave.
+  auto group = [&](int b0, auto refill_tag) {
+    constexpr bool kRefill = decltype(refill_tag)::value;
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) {
       const int b = b0 + i;
@@ -306,53 +371,58 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
       if constexpr (XMODE == XCHUNK) {
         const int chunk = b / a.ci;
         kbase = chunk * a.xc;
-        if (b < nbw && b % a.ci == 0) {
+        if (b % a.ci == 0) {
           __syncthreads();
           chunk_store(a, xc, xs, chunk, tid);
           __syncthreads();
           if ((chunk + 1) * a.xc < a.K) chunk_load(a, xc, chunk + 1, tid);
         }
       }
-      const u32x4_t w = wr[i];
-      const uint16_t sv = sr[i], zv = zr[i];
-      if (b + kDepth < nbw) wload(b + kDepth, wr[i], sr[i], zr[i]);
-      const int kb = b * kWaves + wave;
-      if (b < nbw && kb < nb) {
-        const uint32_t zc = PERCH ? zc_row : zero_constant<DT>(zv);
-        const int kloc = kb * 128 - kbase + 32 * h;
-        u32x4_t bop[4];
+      const u32x4_t w = wr_ring[i];
+      if constexpr (kRefill) wload(b + kDepth, wr_ring[i]);
+      const int kb = b * KG + wk;
+      const bool live = kb < nb;
+      uint32_t zc = zc_row;
+      float sc = 1.f;
+      if constexpr (!PERCH) {
+        // group of block kb: kb / (G / 128) as an exact multiply-shift
+        const int g = (int)(((uint32_t)min(kb, nb - 1) * a.gmul) >> 20);
+        zc = szs[szrow + 2 * g];
+        sc = bitcast<float>(szs[szrow + 2 * g + 1]);
+      }
+      const int kloc = (live ? kb * 128 - kbase : a.xzero) + 32 * h;
+      u32x4_t bop[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bop[t] = dequant_word<DT>(w[t], zc);
-        f32x4_t accg[MB];
+      for (int t = 0; t < 4; ++t) bop[t] = dequant_word<DT>(w[t], zc);
+      f32x4_t accg[MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int m = col + 16 * mb;
-          u32x4_t aop[4];
+      for (int mb = 0; mb < MB; ++mb) {
+        u32x4_t aop[4];
+        const uint16_t *xp = xs + xrow[mb] + kloc;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) aop[t] = u32x4_t{0u, 0u, 0u, 0u};
-          if (m < a.M) {
-            const uint16_t *xp = xs + m * a.xstr + kloc;
+        for (int t = 0; t < 4; ++t) aop[t] = *(const u32x4_t *)(xp + 8 * t);
+        if constexpr (PERCH) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) aop[t] = *(const u32x4_t *)(xp + 8 * t);
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            if constexpr (PERCH) {
-              acc[mb] = mfma_16x16x32<DT>(aop[t], bop[t], acc[mb]);
-            } else {
-              accg[mb] = mfma_16x16x32<DT>(aop[t], bop[t],
-                                           t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : accg[mb]);
-            }
-          }
-        }
-        if constexpr (!PERCH) {
-          const float s = (float)bitcast<_Float16>(sv);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb] += s * accg[mb];
+          for (int t = 0; t < 4; ++t) acc[mb] = mfma_16x16x32<DT>(aop[t], bop[t], acc[mb]);
+        } else {
+          // two independent chains of two, then one add
+          const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t c0 = mfma_16x16x32<DT>(aop[0], bop[0], z4);
+          f32x4_t c1 = mfma_16x16x32<DT>(aop[2], bop[2], z4);
+          c0 = mfma_16x16x32<DT>(aop[1], bop[1], c0);
+          c1 = mfma_16x16x32<DT>(aop[3], bop[3], c1);
+          accg[mb] = c0 + c1;
         }
       }
+      if constexpr (!PERCH) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] += sc * accg[mb];
+      }
     }
-  }
+  };
+  const int last = a.nbw_pad - kDepth;
+  for (int b0 = 0; b0 < last; b0 += kDepth) group(b0, std::true_type{});
+  group(last, std::false_type{});
 
   if constexpr (PERCH) {
 #pragma unroll
@@ -370,24 +440,6 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks)
         zp[mb][ks] = load_partial(a.part + ((size_t)(rbz * kKS + ks) * 16 + jz) * PS + col + 16 * mb);
-    // this wave's rank steps st = wave + 4 i: all loads first
-    const int nst = (a.rank + 3) / 4;
-    float tp[kMaxStepsPerWave][MB][kKS];
-    float bv[kMaxStepsPerWave];
-#pragma unroll
-    for (int i = 0; i < kMaxStepsPerWave; ++i) {
-      const int st = wave + kWaves * i;
-      if (st < nst) {
-        const int j = min(4 * st + h, a.rank - 1);
-        const int rbj = j / 16, jj = j % 16;
-        bv[i] = to_f32<DT>(a.B[(size_t)row * a.rank + j]);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int ks = 0; ks < kKS; ++ks)
-            tp[i][mb][ks] = load_partial(a.part + ((size_t)(rbj * kKS + ks) * 16 + jj) * PS + col + 16 * mb);
-      }
-    }
     float g[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -396,32 +448,56 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
       for (int ks = 0; ks < kKS; ++ks) z += zp[mb][ks];
       g[mb] = gate_sigmoid(z + a.b_gate);
     }
+    // this wave's rank steps st = wk + KG i, four at a time: loads first
+    const int nst = (a.rank + 3) / 4;
+    for (int st0 = wk; st0 < nst; st0 += 4 * KG) {
+      float tp[4][MB][kKS];
+      float bv[4];
 #pragma unroll
-    for (int i = 0; i < kMaxStepsPerWave; ++i) {
-      const int st = wave + kWaves * i;
-      if (st < nst) {
-        const bool jin = 4 * st + h < a.rank;
+      for (int i = 0; i < 4; ++i) {
+        const int st = st0 + KG * i;
+        if (st < nst) {
+          const int j = min(4 * st + h, a.rank - 1);
+          const int rbj = j / 16, jj = j % 16;
+          bv[i] = to_f32<DT>(a.B[(size_t)row * a.rank + j]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          float t = 0.f;
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int ks = 0; ks < kKS; ++ks) t += tp[i][mb][ks];
-          const float u = (jin && col + 16 * mb < a.M) ? g[mb] * t : 0.f;
-          acc[mb] = mfma_16x16x4_f32(u, jin ? bv[i] : 0.f, acc[mb]);
+            for (int ks = 0; ks < kKS; ++ks)
+              tp[i][mb][ks] =
+                  load_partial(a.part + ((size_t)(rbj * kKS + ks) * 16 + jj) * PS + col + 16 * mb);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int st = st0 + KG * i;
+        if (st < nst) {
+          const bool jin = 4 * st + h < a.rank;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            float t = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < kKS; ++ks) t += tp[i][mb][ks];
+            const float u = (jin && col + 16 * mb < a.M) ? g[mb] * t : 0.f;
+            acc[mb] = mfma_16x16x4_f32(u, jin ? bv[i] : 0.f, acc[mb]);
+          }
         }
       }
     }
   }
 
-  if (wave > 0) {
+  // fixed-order sum over the row-block's KG waves
+  if (wk > 0) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) red[wave - 1][mb][lane] = acc[mb];
+    for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
   }
   __syncthreads();
-  if (wave == 0 && n < a.N) {
+  if (wk == 0 && n < a.N) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const f32x4_t v = reduce_waves(acc[mb], red, mb, lane);
+      f32x4_t v = acc[mb];
+#pragma unroll
+      for (int w = 1; w < KG; ++w) v = v + red[wave + w][mb][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 16 * mb + 4 * h + e;
@@ -451,10 +527,10 @@ __device__ void finish(const DecodeArgs &a) {
     __hip_atomic_store(&a.hdr->done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int DT, int MB, bool EC, bool PERCH, int XMODE>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+template <int DT, int MB, bool EC, bool PERCH, int XMODE, int WR>
+__global__ __launch_bounds__(kThreads, XMODE == XWHOLE ? 4 : 2) void decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint16_t xs[];
-  __shared__ f32x4_t red[kWaves - 1][MB][64];
+  f32x4_t(*red)[MB][64] = (f32x4_t(*)[MB][64])((char *)xs + a.red_off);
 
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -462,100 +538,151 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (b < a.producers) {
       produce<DT, MB>(a, b, red, tid >> 6, tid & 63);
     } else {
-      consume<DT, MB, EC, PERCH, XMODE>(a, b - a.producers, xs, red, tid);
+      consume<DT, MB, EC, PERCH, XMODE, WR>(a, b - a.producers, xs, red, tid);
     }
     if (tid == 0) finish(a);
   } else {
-    consume<DT, MB, EC, PERCH, XMODE>(a, b, xs, red, tid);
+    consume<DT, MB, EC, PERCH, XMODE, WR>(a, b, xs, red, tid);
   }
 }
 
-template <int DT, int MB, bool EC, bool PERCH, int XMODE>
+template <int DT, int MB, bool EC, bool PERCH, int XMODE, int WR>
 hipError_t launch_t(const DecodeArgs &a, int grid, size_t lds, hipStream_t s) {
-  auto kern = decode_kernel<DT, MB, EC, PERCH, XMODE>;
+  auto kern = decode_kernel<DT, MB, EC, PERCH, XMODE, WR>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
     attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   kWholeLdsBytes);
+                                   kMaxLds);
   });
   if (attr_err != hipSuccess) return attr_err;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
+template <int DT, int MB, bool EC, bool PERCH, int XMODE>
+hipError_t launch_wr(const DecodeArgs &a, int wr, int grid, size_t lds, hipStream_t s) {
+  switch (wr) {
+    case 1: return launch_t<DT, MB, EC, PERCH, XMODE, 1>(a, grid, lds, s);
+    case 2: return launch_t<DT, MB, EC, PERCH, XMODE, 2>(a, grid, lds, s);
+    case 4: return launch_t<DT, MB, EC, PERCH, XMODE, 4>(a, grid, lds, s);
+    default: return launch_t<DT, MB, EC, PERCH, XMODE, 8>(a, grid, lds, s);
+  }
+}
+
 template <int DT, int MB, bool EC, bool PERCH>
-hipError_t launch_x(const DecodeArgs &a, int xmode, int grid, size_t lds, hipStream_t s) {
-  return xmode == XWHOLE ? launch_t<DT, MB, EC, PERCH, XWHOLE>(a, grid, lds, s)
-                         : launch_t<DT, MB, EC, PERCH, XCHUNK>(a, grid, lds, s);
+hipError_t launch_x(const DecodeArgs &a, const DecodePlan &p, hipStream_t s) {
+  const int grid = p.n_tiles + p.producers;
+  return p.xmode == XWHOLE ? launch_wr<DT, MB, EC, PERCH, XWHOLE>(a, p.wr, grid, p.lds, s)
+                           : launch_wr<DT, MB, EC, PERCH, XCHUNK>(a, p.wr, grid, p.lds, s);
 }
 
 template <int DT, int MB, bool EC>
-hipError_t launch_pc(const DecodeArgs &a, bool perch, int xmode, int grid, size_t lds,
-                     hipStream_t s) {
-  return perch ? launch_x<DT, MB, EC, true>(a, xmode, grid, lds, s)
-               : launch_x<DT, MB, EC, false>(a, xmode, grid, lds, s);
+hipError_t launch_pc(const DecodeArgs &a, const DecodePlan &p, bool perch, hipStream_t s) {
+  return perch ? launch_x<DT, MB, EC, true>(a, p, s) : launch_x<DT, MB, EC, false>(a, p, s);
 }
 
 template <int DT, int MB>
-hipError_t launch_ec(const DecodeArgs &a, bool ec, bool perch, int xmode, int grid, size_t lds,
+hipError_t launch_ec(const DecodeArgs &a, const DecodePlan &p, bool ec, bool perch,
                      hipStream_t s) {
-  return ec ? launch_pc<DT, MB, true>(a, perch, xmode, grid, lds, s)
-            : launch_pc<DT, MB, false>(a, perch, xmode, grid, lds, s);
+  return ec ? launch_pc<DT, MB, true>(a, p, perch, s) : launch_pc<DT, MB, false>(a, p, perch, s);
 }
 
 template <int DT>
-hipError_t launch_mb(const DecodeArgs &a, int mb, bool ec, bool perch, int xmode, int grid,
-                     size_t lds, hipStream_t s) {
-  return mb == 1 ? launch_ec<DT, 1>(a, ec, perch, xmode, grid, lds, s)
-                 : launch_ec<DT, 2>(a, ec, perch, xmode, grid, lds, s);
+hipError_t launch_mb(const DecodeArgs &a, const DecodePlan &p, bool ec, bool perch,
+                     hipStream_t s) {
+  return p.mb == 1 ? launch_ec<DT, 1>(a, p, ec, perch, s) : launch_ec<DT, 2>(a, p, ec, perch, s);
 }
 
 }  // namespace
 
-DecodePlan plan_decode(const LayerDesc &L, int M) {
+// Residency estimate: workgroups of 8 waves per CU that the LDS and the
+// register budget of each staging mode allow.
+static int resident_per_cu(const DecodePlan &p) {
+  const int by_lds = (int)((160 * 1024) / p.lds);
+  const int by_vgpr = p.xmode == XWHOLE ? 2 : 1;  // 8-wave workgroups at 4 (whole) or 2 waves per SIMD
+  const int r = by_lds < by_vgpr ? by_lds : by_vgpr;
+  return r < 1 ? 1 : r;
+}
+
+// One candidate launch shape with wr row-blocks per workgroup; ok == false
+// when it cannot fit the LDS or the staging limits.
+static DecodePlan plan_for(const LayerDesc &L, int M, int wr) {
   DecodePlan p{};
   p.mb = M <= 16 ? 1 : 2;
-  p.n_tiles = (L.N + 15) / 16;
   p.rb_a = L.rank > 0 ? (L.rank + 1 + 15) / 16 : 0;
   p.ks = L.rank > 0 ? kKS : 0;
   p.producers = p.rb_a * p.ks;
   p.nb = (L.K + 127) / 128;
-  p.nbw = (p.nb + kWaves - 1) / kWaves;
+  p.wr = wr;
+  const int kg = kWaves / wr;
+  p.nbw = (p.nb + kg - 1) / kg;
   const int kr = p.nb * 128;
-  const size_t whole = (size_t)M * (kr + 8) * 2;
-  if (whole <= (size_t)kWholeLdsBytes) {
+  const size_t whole = (size_t)M * (kr + 136) * 2;
+  const size_t sz_bytes = L.per_channel ? 0 : (size_t)16 * wr * L.ngroups * 8 + 16;
+  const size_t red_bytes = (size_t)kWaves * p.mb * 64 * 16 + 16;
+  if (whole <= (size_t)kWholeLdsBytes && whole + sz_bytes + red_bytes <= (size_t)kMaxLds) {
     p.xmode = XWHOLE;
     p.ci = 1 << 30;
     p.xc = kr;
-    p.xstr = kr + 8;
-    p.lds = whole;
   } else {
-    // largest chunk of ci iterations (512 * ci columns) within the LDS budget
-    // and at most 8 staged pieces per thread (M * ci <= 32)
-    // pieces per thread: M * 128 * kWaves * ci / 8 / kThreads = M * ci / 4 <= 8
+    // chunk of ci block iterations = 128 * kg * ci columns; each thread stages
+    // at most kChunkPieces 16-byte pieces: M * 128 * kg * ci / 8 <= kChunkPieces * kThreads
+    auto fits = [&](int ci) {
+      return (size_t)M * 16 * kg * ci <= (size_t)kChunkPieces * kThreads &&
+             (size_t)M * (128 * kg * ci + 136) * 2 <= (size_t)kChunkLdsBytes;
+    };
+    if (!fits(1)) {
+      p.ok = false;
+      return p;
+    }
     int ci = 1;
-    while (ci * 2 <= p.nbw && M * ci * 2 <= 32 &&
-           (size_t)M * (128 * kWaves * ci * 2 + 8) * 2 <= (size_t)kChunkLdsBytes)
-      ci *= 2;
+    while (ci * 2 <= p.nbw && fits(ci * 2)) ci *= 2;
     p.xmode = XCHUNK;
     p.ci = ci;
-    p.xc = 128 * kWaves * ci;
-    p.xstr = p.xc + 8;
-    p.lds = (size_t)M * p.xstr * 2;
+    p.xc = 128 * kg * ci;
   }
+  p.xzero = p.xc;
+  p.xstr = p.xc + 128 + 8;
+  p.nbw_pad = (p.nbw + kDepth - 1) / kDepth * kDepth;
+  p.lds = (size_t)M * p.xstr * 2;
+  p.sz_off = (int)((p.lds + 15) / 16 * 16);
+  if (!L.per_channel) p.lds = p.sz_off + (size_t)16 * wr * L.ngroups * 8;
+  p.red_off = (int)((p.lds + 15) / 16 * 16);
+  p.lds = p.red_off + (size_t)kWaves * p.mb * 64 * 16;
+  p.n_tiles = (L.N + 16 * wr - 1) / (16 * wr);
+  p.ok = p.lds <= (size_t)kMaxLds;
   return p;
 }
+
+// Row-blocks per workgroup: the fewest that fit and let the whole grid be
+// resident at once (16 * wr rows share one staged activation); else the
+// largest that fits.
+DecodePlan plan_decode(const LayerDesc &L, int M) {
+  DecodePlan best{};
+  best.ok = false;
+  for (int wr = 1; wr <= 8; wr *= 2) {
+    const DecodePlan p = plan_for(L, M, wr);
+    if (!p.ok) continue;
+    best = p;
+    if (p.n_tiles + p.producers <= 256 * resident_per_cu(p)) break;
+  }
+  return best;
+}
+
+bool decode_supported(const LayerDesc &L, int M) { return plan_decode(L, M).ok; }
 
 size_t decode_workspace_bytes(const LayerDesc &L, int M) {
   if (L.rank == 0) return 0;
   const DecodePlan p = plan_decode(L, M);
+  if (!p.ok) return 0;
   return sizeof(WsHeader) + (size_t)p.producers * 16 * (16 * p.mb) * sizeof(float);
 }
 
 hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
                          void *ws, hipStream_t s) {
   const DecodePlan p = plan_decode(L, M);
+  if (!p.ok) return hipErrorInvalidConfiguration;
   DecodeArgs a{};
   a.qw = L.qw;
   a.scales = L.scales;
@@ -579,12 +706,17 @@ hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint1
   a.ci = p.ci;
   a.xc = p.xc;
   a.xstr = p.xstr;
+  a.xzero = p.xzero;
+  a.nbw_pad = p.nbw_pad;
+  a.sz_off = p.sz_off;
+  // exact for kb * (G / 128) < 2^20, which K <= 131072 guarantees
+  a.gmul = L.per_channel ? 0 : (int)(((1u << 20) + (uint32_t)(L.G / 128) - 1) / (uint32_t)(L.G / 128));
+  a.red_off = p.red_off;
   a.hdr = (WsHeader *)ws;
   a.part = ws ? (float *)((char *)ws + sizeof(WsHeader)) : nullptr;
   const bool ec = L.rank > 0;
-  const int grid = p.n_tiles + p.producers;
-  return dtype == DT_F16 ? launch_mb<DT_F16>(a, p.mb, ec, L.per_channel, p.xmode, grid, p.lds, s)
-                         : launch_mb<DT_BF16>(a, p.mb, ec, L.per_channel, p.xmode, grid, p.lds, s);
+  return dtype == DT_F16 ? launch_mb<DT_F16>(a, p, ec, L.per_channel, s)
+                         : launch_mb<DT_BF16>(a, p, ec, L.per_channel, s);
 }
 
 }  // namespace spear

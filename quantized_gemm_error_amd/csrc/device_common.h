@@ -58,25 +58,39 @@ __device__ __forceinline__ uint32_t zero_constant(uint16_t z_f16_bits) {
   }
 }
 
+// v_and_or_b32: (x & m) | c in one instruction (VOP3; m and c in registers).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
+  return r;
+}
+
 // One packed word (codes q0..q7, lowest nibble first) to the exact values
 // q_i - z in the activation type, as four dwords holding the pairs
 // (q0,q4) (q1,q5) (q2,q6) (q3,q7).  The activation operand that meets these
 // in an MFMA is permuted the same way (permute_8).
 //
-// fp16: (nibble | 0x6400) read as binary16 is 1024 + q exactly; subtracting
-//       1024 + z leaves q - z exactly (an integer of magnitude <= 15).
+// fp16: a low nibble OR 0x6400 read as binary16 is 1024 + q exactly, and a
+//       high nibble (bits 4..7) OR 0x6400 is 1024 + 16 q exactly.  One packed
+//       add of -(1024 + z), or one packed fma by 1/16 with -(64 + z), leaves
+//       q - z exactly (an integer of magnitude <= 15).  zc is the packed pair
+//       -(1024 + z); -(64 + z) is zc + 960.
 // bf16: (nibble | 0x4B000000) read as binary32 is 2^23 + q exactly; after
-//       subtracting 2^23 + z the integer q - z converts to bf16 exactly.
+//       subtracting 2^23 + z (zc holds that fp32 bit pattern) the integer
+//       q - z converts to bf16 exactly.
 template <int DT>
 __device__ __forceinline__ u32x4_t dequant_word(uint32_t w, uint32_t zc) {
   u32x4_t r;
   if constexpr (DT == DT_F16) {
+    const uint32_t lo_mask = 0x000F000Fu, hi_mask = 0x00F000F0u, magic = 0x64006400u;
     const f16x2_t nz = bitcast<f16x2_t>(zc);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t m = ((w >> (4 * t)) & 0x000F000Fu) | 0x64006400u;
-      r[t] = bitcast<uint32_t>(bitcast<f16x2_t>(m) + nz);
-    }
+    const f16x2_t nz64 = nz + f16x2_t{(_Float16)960.0f, (_Float16)960.0f};
+    const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const uint32_t w8 = w >> 8;
+    r[0] = bitcast<uint32_t>(bitcast<f16x2_t>(and_or(w, lo_mask, magic)) + nz);
+    r[1] = bitcast<uint32_t>(bitcast<f16x2_t>(and_or(w, hi_mask, magic)) * sixteenth + nz64);
+    r[2] = bitcast<uint32_t>(bitcast<f16x2_t>(and_or(w8, lo_mask, magic)) + nz);
+    r[3] = bitcast<uint32_t>(bitcast<f16x2_t>(and_or(w8, hi_mask, magic)) * sixteenth + nz64);
   } else {
     const float zf = bitcast<float>(zc);
 #pragma unroll

@@ -41,8 +41,10 @@ struct LayerDesc {
 
 // Derived decode launch geometry.
 struct DecodePlan {
+  bool ok;         // the shape fits the LDS and staging limits
   int mb;          // 16-token blocks (1 or 2)
-  int n_tiles;     // 16-row output tiles
+  int wr;          // 16-row blocks per consumer workgroup
+  int n_tiles;     // consumer workgroups
   int rb_a;        // 16-row blocks of [A; w_g]
   int ks;          // K-splits of the producers
   int producers;   // rb_a * ks (0 when rank == 0)
@@ -50,10 +52,15 @@ struct DecodePlan {
   int xmode;       // 0: all of x staged once; 1: staged in chunks
   int ci, xc;      // chunk: block iterations and K columns
   int xstr;        // LDS row stride of the staged activation (halves)
+  int xzero;       // column of the zero strip in each staged row
+  int nbw_pad;     // block iterations rounded up to a multiple of the ring depth
+  int sz_off;      // byte offset of the scale/zero table in dynamic LDS
+  int red_off;     // byte offset of the wave-reduction buffer in dynamic LDS
   size_t lds;      // dynamic LDS bytes
 };
 
 DecodePlan plan_decode(const LayerDesc &L, int M);
+bool decode_supported(const LayerDesc &L, int M);
 size_t decode_workspace_bytes(const LayerDesc &L, int M);
 size_t prefill_workspace_bytes(const LayerDesc &L, int M);
 
