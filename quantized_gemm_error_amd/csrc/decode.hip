@@ -223,35 +223,47 @@ __device__ __forceinline__ void whole_store(const DecodeArgs &a, const XBatch &x
 // The tile's scales and zero-points as two LDS words per (row, group): the
 // dequant_word zero constant and the scale as fp32.  The tile's rows are
 // consecutive, so their groups form one contiguous range of rows * ngroups
-// elements in each array.
-template <int DT>
-__device__ void stage_sz(const DecodeArgs &a, int n0, int rows, uint32_t *szs, int tid) {
+// elements in each array.  Entries [8 p, 8 p + 8) of the range go to thread
+// p mod kThreads; sz_load fetches one batch (8 entries per thread) into
+// registers and sz_store converts it into LDS, so the first batch can be in
+// flight together with the weight loads.
+struct SzBatch {
+  u16x8_t s, z;
+};
+
+__device__ __forceinline__ void sz_load(const DecodeArgs &a, SzBatch &sb, int n0, int rows, int p) {
   const int ng = a.ngroups;
   const size_t base = (size_t)n0 * ng;
   const size_t end = (size_t)a.N * ng;
   const int cnt = rows * ng;
-  for (int p = tid; 8 * p < cnt; p += kThreads) {
-    const size_t e0 = base + 8 * (size_t)p;
-    u16x8_t sv = {0, 0, 0, 0, 0, 0, 0, 0}, zv = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (e0 + 8 <= end && ((uintptr_t)(a.scales + e0) % 16) == 0 &&
-        ((uintptr_t)(a.zeros + e0) % 16) == 0) {
-      sv = *(const u16x8_t *)(a.scales + e0);
-      zv = *(const u16x8_t *)(a.zeros + e0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (e0 + i < end) {
-          sv[i] = a.scales[e0 + i];
-          zv[i] = a.zeros[e0 + i];
-        }
-      }
-    }
+  sb.s = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  sb.z = sb.s;
+  if (8 * p >= cnt) return;
+  const size_t e0 = base + 8 * (size_t)p;
+  if (e0 + 8 <= end && ((uintptr_t)(a.scales + e0) % 16) == 0 &&
+      ((uintptr_t)(a.zeros + e0) % 16) == 0) {
+    sb.s = *(const u16x8_t *)(a.scales + e0);
+    sb.z = *(const u16x8_t *)(a.zeros + e0);
+  } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (8 * p + i < cnt) {
-        szs[2 * (8 * p + i)] = zero_constant<DT>(zv[i]);
-        szs[2 * (8 * p + i) + 1] = bitcast<uint32_t>((float)bitcast<_Float16>(sv[i]));
+      if (e0 + i < end) {
+        sb.s[i] = a.scales[e0 + i];
+        sb.z[i] = a.zeros[e0 + i];
       }
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void sz_store(const DecodeArgs &a, const SzBatch &sb, int rows, int p,
+                                         uint32_t *szs) {
+  const int cnt = rows * a.ngroups;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (8 * p + i < cnt) {
+      szs[2 * (8 * p + i)] = zero_constant<DT>(sb.z[i]);
+      szs[2 * (8 * p + i) + 1] = bitcast<uint32_t>((float)bitcast<_Float16>(sb.s[i]));
     }
   }
 }
@@ -329,14 +341,25 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
   uint32_t *szs = (uint32_t *)((char *)xs + a.sz_off);
   XChunk xc;
   XBatch xb;
+  SzBatch sb;
   if constexpr (XMODE == XWHOLE) {
     whole_load(a, xb, 0, tid);
   } else {
     chunk_load(a, xc, 0, tid);
   }
+  if constexpr (!PERCH) sz_load(a, sb, n0, 16 * WR, tid);
+  // the weight ring is issued last: the LDS stores below wait only for the
+  // loads issued before it, and each block of the first group waits only
+  // for its own piece
 #pragma unroll
   for (int i = 0; i < kDepth; ++i) wload(i, wr_ring[i]);
-  if constexpr (!PERCH) stage_sz<DT>(a, n0, 16 * WR, szs, tid);
+  if constexpr (!PERCH) {
+    sz_store<DT>(a, sb, 16 * WR, tid, szs);
+    for (int p = tid + kThreads; 8 * p < 16 * WR * a.ngroups; p += kThreads) {
+      sz_load(a, sb, n0, 16 * WR, p);
+      sz_store<DT>(a, sb, 16 * WR, p, szs);
+    }
+  }
   zero_strip(a, xs, tid);
   if constexpr (XMODE == XWHOLE) {
     whole_store(a, xb, xs, 0, tid);
