@@ -20,10 +20,13 @@
 //    u = g * (A x) for its tokens and adds u B^T with fp32 16x16x4 MFMAs; the
 //    eight waves' sums are reduced in a fixed order and y is rounded once.
 //
-// Partial sums travel through agent-scope atomic stores and loads, which are
-// coherent across the XCDs' separate L2 caches on their own, so no wave
-// needs a cache-wide invalidate; only the producers' release (before they
-// count themselves in) writes back their L2.
+// Partial sums travel through agent-scope atomic stores and, on the consumer
+// side, 16-byte buffer loads with the sc1 cache policy (the same access that
+// a relaxed agent-scope atomic load makes), which are coherent across the
+// XCDs' separate L2 caches on their own, so no wave needs a cache-wide
+// invalidate; only the producers' release (before they count themselves in)
+// writes back their L2.  The K-splits of one element sit next to each other,
+// so a consumer gathers them with ks / 4 loads, all in flight at once.
 //
 // Every loop that touches memory has a compile-time shape, so its loads
 // issue back to back and the waits count them exactly.  The last workgroup
@@ -42,7 +45,6 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kDepth = 4;                  // K blocks in flight per wave (one straight-line group)
-constexpr int kKS = kDecodeKSplit;         // producer K-splits
 constexpr uint32_t kSpinLimit = 1u << 20;  // bounded wait for the producers
 constexpr int kWholeLdsBytes = 132 * 1024; // whole-x staging budget
 constexpr int kChunkLdsBytes = 68 * 1024;  // chunked staging budget
@@ -66,9 +68,11 @@ struct DecodeArgs {
   int nbw_pad;     // block iterations rounded up to a multiple of kDepth
   int sz_off;      // byte offset of the scale/zero table in dynamic LDS
   int gmul;        // ceil(2^20 / (G / 128)): kb * gmul >> 20 == kb / (G / 128)
+  int ks;          // producer K-splits per 16-row block of [A; w_g] (a multiple of 4)
+  int part_bytes;  // bytes of the partial-sum array
   int red_off;     // byte offset of the wave-reduction buffer in dynamic LDS
   WsHeader *hdr;
-  float *part;     // [producers][16 rows of A'][16 * MB tokens]
+  float *part;     // [rb_a][16 rows of A'][16 * MB tokens][ks]: a split's sums are contiguous
 };
 
 // Sum of the waves' partial tiles in a fixed order (wave 0's own, then 1..7).
@@ -81,9 +85,10 @@ __device__ __forceinline__ f32x4_t reduce_waves(f32x4_t own, f32x4_t (*red)[MB][
   return v;
 }
 
-__device__ __forceinline__ float load_partial(const float *p) {
-  return bitcast<float>(__hip_atomic_load((const uint32_t *)p, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT));
+// Four consecutive partial sums, read coherently across the XCDs' L2 caches
+// (cache policy sc1, as a relaxed agent-scope atomic load has).
+__device__ __forceinline__ f32x4_t load_partials4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return bitcast<f32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16));
 }
 
 // ---------------------------------------------------------------------------
@@ -92,12 +97,12 @@ __device__ __forceinline__ float load_partial(const float *p) {
 template <int DT, int MB>
 __device__ void produce(const DecodeArgs &a, int p, f32x4_t (*red)[MB][64], int wave, int lane) {
   const int col = lane & 15, h = lane >> 4;
-  const int rb = p / kKS, ksi = p % kKS;
+  const int rb = p / a.ks, ksi = p % a.ks;
   const int j = rb * 16 + col;  // row of [A; w_g]
   const bool jin = j <= a.rank;
   const uint16_t *arow = (j < a.rank) ? a.A + (size_t)j * a.K : a.wg;
   const int nsteps = a.K / 32;
-  const int per = (nsteps + kKS - 1) / kKS;
+  const int per = (nsteps + a.ks - 1) / a.ks;
   const int s0 = ksi * per;
   const int s1 = min(nsteps, s0 + per);
 
@@ -138,13 +143,13 @@ __device__ void produce(const DecodeArgs &a, int p, f32x4_t (*red)[MB][64], int 
   }
   __syncthreads();
   if (wave == 0) {
-    uint32_t *dst = (uint32_t *)a.part + (size_t)p * 16 * (16 * MB);
+    uint32_t *dst = (uint32_t *)a.part + ((size_t)(rb * 16 + col) * (16 * MB)) * a.ks + ksi;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const f32x4_t v = reduce_waves(acc[mb], red, mb, lane);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        __hip_atomic_store(&dst[col * (16 * MB) + 16 * mb + 4 * h + e], bitcast<uint32_t>(v[e]),
+        __hip_atomic_store(&dst[(size_t)(16 * mb + 4 * h + e) * a.ks], bitcast<uint32_t>(v[e]),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -453,59 +458,66 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
   }
 
   if constexpr (EC) {
+    // element (j, m) of [A; w_g] x is the sum of its ks partials at
+    // ((j * 16 MB + m) * ks + [0, ks)) in the partial array
+    const int PS = 16 * MB;
+    const int nst = (a.rank + 3) / 4;  // rank steps of four; this wave takes st = wk + KG i
+    // B for the wave's first rank step does not depend on the producers
+    float b_first = 0.f;
+    if (wk < nst) b_first = to_f32<DT>(a.B[(size_t)row * a.rank + min(4 * wk + h, a.rank - 1)]);
     wait_producers(a, tid);
-    const int PS = 16 * MB;  // token stride of a partial row
-    // gate of this lane's A-operand token (m = col + 16 mb)
-    const int rbz = a.rank / 16, jz = a.rank % 16;
-    float zp[MB][kKS];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks)
-        zp[mb][ks] = load_partial(a.part + ((size_t)(rbz * kKS + ks) * 16 + jz) * PS + col + 16 * mb);
+    const __amdgpu_buffer_rsrc_t pr =
+        __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
+    const int kq = a.ks / 4;
     float g[MB];
+    // one rank step; the first also gathers the gate row j = rank, with its
+    // loads in flight together with the step's own
+    auto step = [&](int st, float bval, auto gate_tag) {
+      constexpr bool kGate = decltype(gate_tag)::value;
+      const int j = min(4 * st + h, a.rank - 1);
+      float t[MB], z[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float z = 0.f;
+      for (int mb = 0; mb < MB; ++mb) t[mb] = z[mb] = 0.f;
+      for (int q0 = 0; q0 < kq; q0 += 2) {
+        f32x4_t tv[MB][2], zv[MB][2];
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) z += zp[mb][ks];
-      g[mb] = gate_sigmoid(z + a.b_gate);
-    }
-    // this wave's rank steps st = wk + KG i, four at a time: loads first
-    const int nst = (a.rank + 3) / 4;
-    for (int st0 = wk; st0 < nst; st0 += 4 * KG) {
-      float tp[4][MB][kKS];
-      float bv[4];
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int st = st0 + KG * i;
-        if (st < nst) {
-          const int j = min(4 * st + h, a.rank - 1);
-          const int rbj = j / 16, jj = j % 16;
-          bv[i] = to_f32<DT>(a.B[(size_t)row * a.rank + j]);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int ks = 0; ks < kKS; ++ks)
-              tp[i][mb][ks] =
-                  load_partial(a.part + ((size_t)(rbj * kKS + ks) * 16 + jj) * PS + col + 16 * mb);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int st = st0 + KG * i;
-        if (st < nst) {
-          const bool jin = 4 * st + h < a.rank;
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            float t = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < kKS; ++ks) t += tp[i][mb][ks];
-            const float u = (jin && col + 16 * mb < a.M) ? g[mb] * t : 0.f;
-            acc[mb] = mfma_16x16x4_f32(u, jin ? bv[i] : 0.f, acc[mb]);
+          for (int qq = 0; qq < 2; ++qq) {
+            const int q = min(q0 + qq, kq - 1);
+            tv[mb][qq] = load_partials4(pr, (((j * PS + col + 16 * mb) * a.ks) + 4 * q) * 4);
+            if constexpr (kGate)
+              zv[mb][qq] = load_partials4(pr, (((a.rank * PS + col + 16 * mb) * a.ks) + 4 * q) * 4);
           }
-        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            if (q0 + qq < kq) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                t[mb] += tv[mb][qq][e];
+                if constexpr (kGate) z[mb] += zv[mb][qq][e];
+              }
+            }
+          }
       }
+      if constexpr (kGate) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) g[mb] = gate_sigmoid(z[mb] + a.b_gate);
+      }
+      const bool jin = 4 * st + h < a.rank;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const float u = (jin && col + 16 * mb < a.M) ? g[mb] * t[mb] : 0.f;
+        acc[mb] = mfma_16x16x4_f32(u, jin ? bval : 0.f, acc[mb]);
+      }
+    };
+    if (wk < nst) {
+      step(wk, b_first, std::true_type{});
+      for (int st = wk + KG; st < nst; st += KG)
+        step(st, to_f32<DT>(a.B[(size_t)row * a.rank + min(4 * st + h, a.rank - 1)]),
+             std::false_type{});
     }
   }
 
@@ -619,6 +631,16 @@ hipError_t launch_mb(const DecodeArgs &a, const DecodePlan &p, bool ec, bool per
 
 }  // namespace
 
+// K-splits of the compensator producers: enough that every producer wave
+// covers its split in one pass of eight 32-wide steps (8 waves x 8 steps =
+// 2048 columns per split), rounded up to a multiple of 4 so that the
+// consumers read whole 16-byte groups of partials; at least 4, at most 16.
+static int decode_ksplit(int K) {
+  const int need = (K / 32 + 63) / 64;
+  const int ks = (need + 3) / 4 * 4;
+  return ks < 4 ? 4 : (ks > 16 ? 16 : ks);
+}
+
 // Residency estimate: workgroups of 8 waves per CU that the LDS and the
 // register budget of each staging mode allow.
 static int resident_per_cu(const DecodePlan &p) {
@@ -634,7 +656,7 @@ static DecodePlan plan_for(const LayerDesc &L, int M, int wr) {
   DecodePlan p{};
   p.mb = M <= 16 ? 1 : 2;
   p.rb_a = L.rank > 0 ? (L.rank + 1 + 15) / 16 : 0;
-  p.ks = L.rank > 0 ? kKS : 0;
+  p.ks = L.rank > 0 ? decode_ksplit(L.K) : 0;
   p.producers = p.rb_a * p.ks;
   p.nb = (L.K + 127) / 128;
   p.wr = wr;
@@ -735,6 +757,8 @@ hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint1
   // exact for kb * (G / 128) < 2^20, which K <= 131072 guarantees
   a.gmul = L.per_channel ? 0 : (int)(((1u << 20) + (uint32_t)(L.G / 128) - 1) / (uint32_t)(L.G / 128));
   a.red_off = p.red_off;
+  a.ks = p.ks;
+  a.part_bytes = (int)((size_t)p.producers * 16 * (16 * p.mb) * sizeof(float));
   a.hdr = (WsHeader *)ws;
   a.part = ws ? (float *)((char *)ws + sizeof(WsHeader)) : nullptr;
   const bool ec = L.rank > 0;

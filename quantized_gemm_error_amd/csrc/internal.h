@@ -27,7 +27,6 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) == 2048, "workspace header is 2048 bytes");
 
-constexpr int kDecodeKSplit = 4;  // K-splits of the decode compensator producers
 
 // Everything a launcher needs, already validated.
 struct LayerDesc {
