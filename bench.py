@@ -37,6 +37,7 @@ METRIC = "decode GB/s & prefill TFLOP/s (% roofline), compensator overhead vs pl
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 ROTATION_BYTES = 1 << 30
+COPY_CAL_BYTES = 256 << 20
 
 
 def log(msg: str) -> None:
@@ -145,17 +146,22 @@ def capture_graphs(torch, fn_per_phase, n_phases, stream):
 
 
 def timed_decode_steps(torch, wl, steps, warmup):
-    """Replay captured steps; HIP events on the stream time each kernel class.
+    """Replay captured steps back to back; HIP events on the stream time the run.
 
-    A step is two graphs replayed back to back on one stream: the launches of
-    the dominant kernel (one token block, M <= 16: nine calls) and the M = 32
-    launches (three calls).  Events recorded on the same stream before, between
-    and after the two replays give each class's device time per step.
+    One graph holds a whole rotation of steps (each step's twelve calls, on
+    the next copies of the layers); the timed region replays it, then
+    per-step graphs for the remainder, exactly `steps` steps in all, with
+    events only before the first and after the last launch, as a serving
+    loop that captures its decode steps would run.  Two more passes of the same length replay only one kernel class
+    each (the dominant one-token-block launches, M <= 16: nine calls a step;
+    and the M = 32 launches: three) to give each class's device time per
+    launch.
     """
     stream = torch.cuda.Stream()
     n_calls = len(wl.calls)
     n_phases = wl.n_sets // int(np.gcd(wl.n_sets, n_calls))
-    classes = {"one_block": [c for c in range(n_calls) if wl.calls[c][1] <= 16],
+    classes = {"all": list(range(n_calls)),
+               "one_block": [c for c in range(n_calls) if wl.calls[c][1] <= 16],
                "two_blocks": [c for c in range(n_calls) if wl.calls[c][1] > 16]}
 
     def issue_class(ph, cls):
@@ -165,38 +171,46 @@ def timed_decode_steps(torch, wl, steps, warmup):
 
     with torch.cuda.stream(stream):
         for ph in range(n_phases):          # eager warm-up of every layer copy
-            for cls in classes:
-                issue_class(ph, cls)
+            issue_class(ph, "all")
     torch.cuda.synchronize()
-    graphs = []
-    for ph in range(n_phases):
-        pair = []
-        for cls in classes:
+    # per class: one graph holding a whole rotation (n_phases steps), and one
+    # graph per phase for a remainder of fewer steps
+    full, per_phase = {}, {}
+    for cls in classes:
+        per_phase[cls] = []
+        for ph in range(n_phases):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 issue_class(ph, cls)
-            pair.append(g)
-        graphs.append(pair)
-    for i in range(warmup):
-        for g in graphs[i % n_phases]:
-            g.replay()
+            per_phase[cls].append(g)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for ph in range(n_phases):
+                issue_class(ph, cls)
+        full[cls] = g
+
+    def run(cls, n):
+        q, r = divmod(n, n_phases)
+        with torch.cuda.stream(stream):    # replay() runs on the current stream
+            for _ in range(q):
+                full[cls].replay()
+            for ph in range(r):
+                per_phase[cls][ph].replay()
+
+    run("all", warmup)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        for i in range(steps):
-            ga, gb = graphs[i % n_phases]
-            e0, e1, e2 = evs[i]
-            e0.record(stream)
-            ga.replay()
-            e1.record(stream)
-            gb.replay()
-            e2.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = evs[0][0].elapsed_time(evs[-1][2])
-    cls_ms = {"one_block": sum(e[0].elapsed_time(e[1]) for e in evs),
-              "two_blocks": sum(e[1].elapsed_time(e[2]) for e in evs)}
+    out = {}
+    for cls in classes:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        run(cls, steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[cls] = (e0.elapsed_time(e1), time.perf_counter() - t0)
+    total_ms, wall = out["all"]
+    cls_ms = {c: out[c][0] for c in ("one_block", "two_blocks")}
     return total_ms, wall, cls_ms, classes
 
 
@@ -320,6 +334,184 @@ def cpu_baseline(budget_s=12.0):
                       f"BLAS uses {cores} threads"}
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (CPU only): kernel-trace statistics and HBM traffic
+# ---------------------------------------------------------------------------
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_llama7b_traffic.json")
+DOMINANT_SOURCES = ("quantized_gemm_error_amd/csrc/decode.hip",
+                    "quantized_gemm_error_amd/csrc/device_common.h",
+                    "quantized_gemm_error_amd/csrc/internal.h")
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "
+             "python3 bench.py --steps 300 --warmup 10 --no-extra --no-cpu")
+PMC_CMD = ("rocprofv3 --pmc {counter} -f csv -d gpurun_out/prof_{tag} -o run -- "
+           "python3 bench.py --steps 10 --warmup 2 --no-extra --no-cpu --copy-calibration")
+
+
+def dominant_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DOMINANT_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _decode_template_args(name):
+    """(DT, MB, EC, PERCH, XMODE, WR) of a decode_kernel instantiation, else None."""
+    key = "decode_kernel<"
+    if key not in name:
+        return None
+    inner = name[name.index(key) + len(key):].split(">")[0]
+    return tuple(t.strip() for t in inner.split(","))
+
+
+def _is_dominant(name):
+    t = _decode_template_args(name)
+    return t is not None and t[1] == "1" and t[2] == "true"
+
+
+def _short(name):
+    return name.replace("spear::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def measured_traffic():
+    """HBM bytes per dominant launch from the committed counter summary, or None if the
+    kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    if rec.get("kernel_sources_sha256") != dominant_sources_sha256():
+        return None, "kernel sources changed since the counters were taken"
+    return rec.get("traffic_bytes_per_launch"), None
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
+    import csv
+    import statistics
+
+    def rows(path):
+        with open(path, newline="") as f:
+            return list(csv.DictReader(f))
+
+    os.makedirs(out_dir, exist_ok=True)
+    # ---- kernel trace --------------------------------------------------------
+    stats = rows(os.path.join(trace_dir, "run_kernel_stats.csv"))
+    trace = rows(os.path.join(trace_dir, "run_kernel_trace.csv"))
+    trace.sort(key=lambda r: int(r["Dispatch_Id"]))
+    dom = [r for r in trace if _is_dominant(r["Kernel_Name"])]
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in dom]
+    # start-to-start spacing of back-to-back dominant dispatches (the graph's cadence)
+    spacing = []
+    for a, b in zip(trace, trace[1:]):
+        if _is_dominant(a["Kernel_Name"]) and _is_dominant(b["Kernel_Name"]) and \
+                int(b["Dispatch_Id"]) == int(a["Dispatch_Id"]) + 1:
+            spacing.append((int(b["Start_Timestamp"]) - int(a["Start_Timestamp"])) / 1e3)
+    bench_line = None
+    log_path = trace_dir.rstrip("/") + ".log"
+    if os.path.exists(log_path):
+        for ln in open(log_path):
+            if ln.startswith("{"):
+                bench_line = json.loads(ln)
+    # the pass that replays only the dominant launches: the longest run of
+    # consecutive dominant dispatches; its span per launch is what HIP events
+    # around that pass measure
+    runs, cur = [], []
+    for r in trace:
+        if _is_dominant(r["Kernel_Name"]) and (not cur or int(r["Dispatch_Id"]) == int(cur[-1]["Dispatch_Id"]) + 1):
+            cur.append(r)
+        else:
+            if cur:
+                runs.append(cur)
+            cur = [r] if _is_dominant(r["Kernel_Name"]) else []
+    if cur:
+        runs.append(cur)
+    longest = max(runs, key=len)
+    span_us = (int(longest[-1]["End_Timestamp"]) - int(longest[0]["Start_Timestamp"])) / 1e3 / len(longest)
+    agree = ["", f"- dominant-only pass: {len(longest)} consecutive dispatches, span per launch "
+                 f"{span_us:.3f} us, mean duration {statistics.mean((int(r['End_Timestamp']) - int(r['Start_Timestamp'])) / 1e3 for r in longest):.3f} us"]
+    if bench_line is not None:
+        b_us = bench_line["roofline"]["avg_launch_us"]
+        agree += ["", f"bench.py's own figure in the same run (HIP events around that pass): {b_us:.3f} us "
+                      f"per launch; trace span / bench = {span_us / b_us:.3f}."]
+    lines = ["# decode_kernel, Llama-7B decode projections: rocprofv3 kernel trace", "",
+             "Command (repository root, one MI355X):", "", "    " + TRACE_CMD, "",
+             "Dominant kernel: decode_kernel with one 16-token block (M <= 16) and the "
+             "compensator, all its instantiations (the three shapes select the row-block "
+             "width and the staging mode).", "",
+             f"- dispatches: {len(dom)}",
+             f"- mean kernel duration: {statistics.mean(dur):.3f} us (median {statistics.median(dur):.3f})",
+             f"- mean start-to-start spacing of consecutive dispatches: "
+             f"{statistics.mean(spacing):.3f} us over {len(spacing)} pairs" if spacing else "- no pairs",
+             *agree,
+             "", "rocprofv3 stamps a kernel's start when the previous one in the stream ends, so "
+                 "for back-to-back launches its duration is the launch-to-launch time.",
+             "", "Per kernel (rocprofv3 --stats):", "",
+             "| kernel | calls | average us | min us | max us | % of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{_short(r['Name'])[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {r['Percentage']} |")
+    with open(os.path.join(out_dir, "decode_kernel_llama7b_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # ---- counters --------------------------------------------------------------
+    def counter_pass(d):
+        rs = rows(os.path.join(d, "run_counter_collection.csv"))
+        rs.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = [r for r in rs if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")][-3:]
+        cal = statistics.mean(float(r["Counter_Value"]) for r in copies)  # KiB per 256 MiB copy
+        scale = cal / (COPY_CAL_BYTES / 1024.0)
+        per = {}
+        for r in rs:
+            if _is_dominant(r["Kernel_Name"]):
+                per.setdefault((_short(r["Kernel_Name"]), r["Grid_Size"]), []).append(float(r["Counter_Value"]))
+        allv = [v for vs in per.values() for v in vs]
+        return scale, cal, per, statistics.mean(allv), len(allv)
+
+    f_scale, f_cal, f_per, f_mean, f_n = counter_pass(fetch_dir)
+    w_scale, w_cal, w_per, w_mean, w_n = counter_pass(write_dir)
+    fetch_b = f_mean * 1024.0 / f_scale
+    write_b = w_mean * 1024.0 / w_scale
+    traffic = fetch_b + write_b
+    lines = ["# decode_kernel, Llama-7B decode projections: HBM traffic from counters", "",
+             "Commands (repository root, one MI355X, one counter per pass):", "",
+             "    " + PMC_CMD.format(counter="FETCH_SIZE", tag="fetch"),
+             "    " + PMC_CMD.format(counter="WRITE_SIZE", tag="write"), "",
+             "Scale: the last three dispatches of each pass are device-to-device copies of "
+             f"{COPY_CAL_BYTES >> 20} MiB (`__amd_rocclr_copyBuffer`).", "",
+             f"- FETCH_SIZE per copy: {f_cal:.1f} KiB -> scale {f_scale:.5f}",
+             f"- WRITE_SIZE per copy: {w_cal:.1f} KiB -> scale {w_scale:.5f}", "",
+             f"Dominant kernel (M <= 16, compensated), mean over {f_n} / {w_n} dispatches:", "",
+             f"- FETCH_SIZE {f_mean:.1f} KiB -> {fetch_b / 1e6:.3f} MB read",
+             f"- WRITE_SIZE {w_mean:.1f} KiB -> {write_b / 1e6:.3f} MB written",
+             f"- traffic per launch: {traffic / 1e6:.3f} MB", "",
+             "| instantiation | grid (threads) | dispatches | FETCH KiB | WRITE KiB | scaled MB |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for k in sorted(f_per):
+        fv, wv = f_per[k], w_per.get(k, [0.0])
+        fm, wm = statistics.mean(fv), statistics.mean(wv)
+        lines.append(f"| `{k[0]}` | {k[1]} | {len(fv)} | {fm:.1f} | {wm:.1f} | "
+                     f"{(fm / f_scale + wm / w_scale) * 1024 / 1e6:.3f} |")
+    with open(os.path.join(out_dir, "decode_kernel_llama7b_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    rec = {"kernel": "decode_kernel, M <= 16, compensated (all instantiations)",
+           "kernel_sources_sha256": dominant_sources_sha256(),
+           "traffic_bytes_per_launch": int(round(traffic)),
+           "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b)),
+           "fetch_scale": round(f_scale, 6), "write_scale": round(w_scale, 6),
+           "dispatches": [f_n, w_n],
+           "commands": [PMC_CMD.format(counter="FETCH_SIZE", tag="fetch"),
+                        PMC_CMD.format(counter="WRITE_SIZE", tag="write")]}
+    with open(TRAFFIC_FILE if out_dir == os.path.dirname(TRAFFIC_FILE)
+              else os.path.join(out_dir, os.path.basename(TRAFFIC_FILE)), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,7 +519,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extra", action="store_true", help="skip overhead/prefill context")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 256 MiB device to device three times: the "
+                         "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summaries from rocprofv3 CSV output (no GPU)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, out_dir=os.path.join(ROOT, "profiles"))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
@@ -349,14 +549,25 @@ def main():
     value = wl.step_bytes * args.steps / (total_ms * 1e-3) / 1e9
     log(f"decode: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s")
 
+    if args.copy_calibration:
+        src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # dominant kernel: decode_kernel, one token block (M <= 16), compensated, group-wise
     dom_calls = [wl.calls[c] for c in classes["one_block"]]
     dom_bytes = sum(call_bytes(wl.shapes[si][1], wl.shapes[si][0], wl.G, wl.r, M) for si, M in dom_calls)
     n_launch = len(dom_calls) * args.steps
     dom_ms = cls_ms["one_block"]
     achieved = dom_bytes * args.steps / (dom_ms * 1e-3) / 1e9
+    traffic, traffic_note = measured_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                "traffic_note": traffic_note,
                 "kernel": "decode_kernel<f16, one 16-token block, compensated, group-wise>",
                 "avg_launch_us": round(dom_ms / n_launch * 1e3, 3), "launches_timed": n_launch,
                 "bytes_per_launch_avg": int(dom_bytes / len(dom_calls))}
