@@ -338,7 +338,9 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
   auto wload = [&](int b, u32x4_t &w) {
     const int kb = min(b * KG + wk, nb - 1);
     const int off = (kb * 128 + 32 * h < a.K) ? kb * 16 + 4 * h : 0;
-    w = *(const u32x4_t *)(wrow + off);
+    // read once per call: non-temporal, so the stream does not displace the
+    // layer's small operands from the caches
+    w = __builtin_nontemporal_load((const u32x4_t *)(wrow + off));
   };
 
   // activation loads first, then the weight ring, so that storing the

@@ -233,6 +233,7 @@ PREFILL_CASES = [
     (384, 768, 256, 32, 257, "bf16", True, True),  # G = 256, bf16
     (128, 256, 128, 0, 100, "f16", False, True),   # rank 0
     (64, 128, 128, 4, 33, "f16", False, True),     # M just above the decode range
+    (200, 512, 128, 100, 77, "f16", False, True),  # rank 100: padded U rows, 7 row blocks of [A; w_g]
 ]
 
 
@@ -276,6 +277,30 @@ def test_decode_and_prefill_agree_and_dispatch():
     assert_close(gpu_y_f64(yp, "f16"), ref[:32], "prefill")
     assert torch.equal(yl32.view(torch.int16), yd.view(torch.int16))     # M = 32 -> decode
     assert torch.equal(yl48.view(torch.int16), yp48.view(torch.int16))   # M = 48 -> prefill
+
+
+def test_workspace_shared_by_prefill_and_decode():
+    """One workspace, sized for the largest call, reused by prefill (serial and
+    concurrent) and decode calls of many token counts in any order."""
+    note("workspace shared by prefill and decode")
+    hl, xb, lay, x = _setup(264, 1536, 128, 40, seed=21, M=300, outliers=True)
+    ws = spear.new_workspace(lay, 300)
+    ref = oracle_y(hl, xb)
+    aux = torch.cuda.Stream()
+    outs = []
+    for it, M in enumerate([300, 7, 129, 32, 1, 64, 300, 16, 17, 2]):
+        xm = x[:M].contiguous()
+        if M <= 32 and it % 2 == 0:
+            y = spear.spear_linear_decode(lay, xm, workspace=ws)
+        elif it % 3 == 0:
+            y = spear.spear_linear_prefill(lay, xm, workspace=ws, aux_stream=aux)
+        else:
+            y = spear.spear_linear_prefill(lay, xm, workspace=ws)
+        outs.append((it, M, y))
+    torch.cuda.synchronize()
+    for it, M, y in outs:
+        assert_close(gpu_y_f64(y, "f16"), ref[:M], f"call {it} M={M}")
+    assert spear.spear_workspace_flags(ws) == 0
 
 
 # ---------------------------------------------------------------------------
