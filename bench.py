@@ -262,7 +262,7 @@ def decode_overhead(torch, wl_ec, wl_r0):
 def prefill_context(torch, device):
     """Llama-7B prefill, M = 2048, bf16: TFLOP/s of the serial schedule (compensator,
     then the GEMM with the compensator in its epilogue), of the concurrent schedule
-    (compensator on an aux stream, merge after the join), and of rank 0."""
+    (compensator on an aux stream, merge after the join), and of rank 0 (same workspace)."""
     from quantized_gemm_error_amd import spear, synth
     w = synth.WORKLOADS["llama7b-prefill"]
     M = w["tokens"][0]
@@ -284,7 +284,7 @@ def prefill_context(torch, device):
             spear.spear_linear_prefill(lay, x, y=y, workspace=ws, main_stream=s, aux_stream=aux)
 
         def run_r0(_i, s):
-            spear.spear_linear_prefill(lay0, x, y=y, main_stream=s)
+            spear.spear_linear_prefill(lay0, x, y=y, workspace=ws, main_stream=s)
         t_s = graph_call_time_ms(torch, run_serial, 4)
         t_c = graph_call_time_ms(torch, run_conc, 4)
         t_r0 = graph_call_time_ms(torch, run_r0, 4)
@@ -298,6 +298,162 @@ def prefill_context(torch, device):
             "overhead_pct_concurrent": round(100.0 * (t_c / t_r0 - 1.0), 2),
         }
         del lay, lay0, x, y, ws
+    return out
+
+
+def random_layer(torch, N, K, G, r, device, gen, act):
+    """A 4-bit layer drawn directly on the device, for timing only (values do not change
+    the work): random packed codes, fp16 scales in [0.001, 0.005), integer zero-points,
+    A, B ~ N(0, 0.01), w_g ~ N(0, 0.05)."""
+    from quantized_gemm_error_amd.spear import SpearLayer
+    ng = K // G
+    qw = torch.randint(-2**31, 2**31 - 1, (N, K // 8), dtype=torch.int32, device=device, generator=gen)
+    sc = (torch.rand((N, ng), device=device, generator=gen) * 0.004 + 0.001).to(torch.float16)
+    zp = torch.randint(0, 16, (N, ng), device=device, generator=gen).to(torch.float16)
+    lay = SpearLayer(N=N, K=K, group_size=G, qweight=qw, scales=sc, zeros=zp, rank=r)
+    if r > 0:
+        lay.A = (torch.randn((r, K), device=device, generator=gen) * 0.01).to(act)
+        lay.B = (torch.randn((N, r), device=device, generator=gen) * 0.01).to(act)
+        lay.w_gate = (torch.randn((K,), device=device, generator=gen) * 0.05).to(act)
+    return lay
+
+
+def llama70b_context(torch, device):
+    """Llama-70B layer projections, per-channel 4-bit, rank 64, fp16, M in {1, 64, 256}
+    through the phase-aware entry point; layer copies rotate over >= 1 GiB."""
+    from quantized_gemm_error_amd import spear, synth
+    w = synth.WORKLOADS["llama70b-layer"]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w["seed"])
+    r = w["rank"]
+    base = [random_layer(torch, N, K, K, r, device, gen, torch.float16) for K, N in w["shapes"]]
+    set_bytes = sum(layer_bytes(l) for l in base)
+    n_sets = max(2, -(-ROTATION_BYTES // set_bytes))
+    sets = [base] + [[clone_layer(l) for l in base] for _ in range(n_sets - 1)]
+    out = {}
+    for si, (K, N) in enumerate(w["shapes"]):
+        for M in w["tokens"]:
+            x = torch.randn((M, K), device=device, generator=gen).to(torch.float16)
+            y = torch.empty((M, N), dtype=torch.float16, device=device)
+            ws = spear.new_workspace(base[si], M)
+            t_ec = graph_call_time_ms(
+                torch, lambda i, s: spear.spear_linear(sets[i % n_sets][si], x, y=y, workspace=ws,
+                                                       main_stream=s), n_sets)
+            t_r0 = graph_call_time_ms(
+                torch, lambda i, s: spear.spear_linear(sets[i % n_sets][si].without_compensator(), x,
+                                                       y=y, workspace=ws, main_stream=s), n_sets)
+            b, f = call_bytes(N, K, K, r, M), call_flops(N, K, r, M)
+            gbs, tfs = b / (t_ec * 1e-3) / 1e9, f / (t_ec * 1e-3) / 1e12
+            out[f"{K}->{N} M={M}"] = {
+                "phase": "decode" if M <= 32 else "prefill",
+                "us_ec": round(t_ec * 1e3, 2), "us_r0": round(t_r0 * 1e3, 2),
+                "overhead_pct": round(100.0 * (t_ec / t_r0 - 1.0), 2),
+                "GBps_ec": round(gbs, 1), "hbm_frac_ec": round(gbs / HBM_PEAK_GBS, 4),
+                "TFLOPs_ec": round(tfs, 1), "mfma_frac_ec": round(tfs / MFMA_F16_PEAK_TFLOPS, 4)}
+            del ws, x, y
+    del sets, base
+    torch.cuda.empty_cache()
+    return {"layer_copies": n_sets, "calls": out}
+
+
+def serving_context(torch, device):
+    """Chunked serving over a 32-block stack of the three 7B projections (random-init g128
+    4-bit, compensators of rank 32 on 4 seeded blocks).  A step is one prefill chunk of C
+    tokens plus 32 decode tokens through every linear.  A latency table measured per
+    (shape, compensated or not, C or decode) predicts the step time; the chunk selector
+    picks C for each budget; the chosen step is then run and timed."""
+    from quantized_gemm_error_amd import spear, synth
+    w = synth.WORKLOADS["llama7b-stack-serving"]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w["seed"])
+    shapes, chunks, n_dec = list(w["shapes"]), list(w["chunks"]), w["decode_tokens"]
+    ec_set = {int(b) for b in synth.ec_block_indices(w["blocks"], w["ec_blocks"], w["seed"])}
+    stack = [[random_layer(torch, N, K, w["group_size"], w["rank"] if b in ec_set else 0, device, gen,
+                           torch.float16) for K, N in shapes] for b in range(w["blocks"])]
+    maxC = max(chunks)
+    xs = {K: torch.randn((maxC, K), device=device, generator=gen).to(torch.float16)
+          for K in {k for k, _ in shapes}}
+    ys = {N: torch.empty((maxC, N), dtype=torch.float16, device=device) for N in {n for _, n in shapes}}
+    # one workspace for every linear: the calls are ordered on one stream
+    b_ec = min(ec_set)
+    nws = max(spear.spear_workspace_bytes(stack[b_ec][si], maxC) for si in range(len(shapes)))
+    wbuf = torch.zeros(nws + 256, dtype=torch.uint8, device=device)
+    ws = wbuf[(-wbuf.data_ptr()) % 256:][:nws]
+
+    def call(b, si, M, s):
+        K, N = shapes[si]
+        spear.spear_linear(stack[b][si], xs[K][:M], y=ys[N][:M], workspace=ws, main_stream=s)
+
+    # latency table: each entry timed over the stack's blocks of that kind (cold weights)
+    kinds = {True: sorted(ec_set), False: [b for b in range(w["blocks"]) if b not in ec_set]}
+    lut = {}
+    for si in range(len(shapes)):
+        for ec, blocks in kinds.items():
+            for M in chunks + [n_dec]:
+                lut[(si, ec, M)] = graph_call_time_ms(
+                    torch, lambda i, s: call(blocks[i % len(blocks)], si, M, s), len(blocks), reps=3)
+
+    def predicted(C):
+        return sum(lut[(si, b in ec_set, C)] + lut[(si, b in ec_set, n_dec)]
+                   for b in range(w["blocks"]) for si in range(len(shapes)))
+
+    pred = [predicted(C) for C in chunks]
+    stream = torch.cuda.Stream()
+    out = []
+    for budget in (1.0, 2.0, 4.0, 8.0, 16.0, w["budget_ms"]):
+        C, violated = spear.spear_select_chunk(chunks, pred, budget)
+
+        def step(_i, s, C=C):
+            for b in range(w["blocks"]):
+                for si in range(len(shapes)):
+                    call(b, si, C, s)
+                    call(b, si, n_dec, s)
+        t = graph_call_time_ms(torch, step, 1, reps=3)
+        out.append({"budget_ms": budget, "chunk": C, "violated": bool(violated),
+                    "predicted_ms": round(pred[chunks.index(C)], 3), "measured_ms": round(t, 3),
+                    "slo_met": bool(t <= budget)})
+    ec_bytes = sum(layer_bytes(stack[b][si]) - layer_bytes(stack[b][si].without_compensator())
+                   for b in ec_set for si in range(len(shapes)))
+    all_bytes = sum(layer_bytes(l) for blk in stack for l in blk)
+    del stack, xs, ys, ws, wbuf
+    torch.cuda.empty_cache()
+    return {"ec_blocks": sorted(ec_set), "predicted_step_ms": dict(zip(map(str, chunks), [round(p, 3) for p in pred])),
+            "compensator_memory_pct": round(100.0 * ec_bytes / (all_bytes - ec_bytes), 3),
+            "budgets": out}
+
+
+def ceilings(torch, device):
+    """Context only: a 1 GiB device-to-device copy, and hipBLASLt bf16 GEMMs at the prefill
+    shapes (dense bf16 weights, torch.matmul)."""
+    from quantized_gemm_error_amd import synth
+    out = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["d2d_copy_GBps"] = round(5 * 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    gemm = {}
+    for K, N in synth.LLAMA7B_SHAPES:
+        a = torch.randn((2048, K), device=device).to(torch.bfloat16)
+        bt = torch.randn((N, K), device=device).to(torch.bfloat16).t().contiguous()  # [K][N]
+        torch.matmul(a, bt)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            torch.matmul(a, bt)
+        e1.record()
+        torch.cuda.synchronize()
+        gemm[f"{K}->{N} M=2048"] = round(10 * 2 * 2048 * K * N / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+        del a, bt
+    out["hipblaslt_bf16_dense_TFLOPs"] = gemm
+    torch.cuda.empty_cache()
     return out
 
 
@@ -596,6 +752,12 @@ def main():
         del wl
         torch.cuda.empty_cache()
         extra["prefill_llama7b_bf16_M2048"] = prefill_context(torch, dev)
+        log("llama-70B layer")
+        extra["llama70b_layer_fp16"] = llama70b_context(torch, dev)
+        log("serving stack")
+        extra["serving_stack_7b"] = serving_context(torch, dev)
+        log("ceilings")
+        extra["ceilings"] = ceilings(torch, dev)
     cpu = None
     if not args.no_cpu:
         log("cpu oracle baseline")

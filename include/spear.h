@@ -107,8 +107,15 @@ typedef struct spear_layer {
  * spear_linear need for this layer for any call with 1..M tokens.
  * Returns 0 when the layer or M is invalid.  The workspace is caller-owned
  * device memory, 256-byte aligned, and must be ZEROED ONCE before its first
- * use; every call leaves it ready for the next one.  Calls that may run
- * concurrently (different streams) need different workspaces.
+ * use; every call leaves it ready for the next one.  One workspace may serve
+ * several layers if it is at least the largest of their sizes: its counters
+ * sit at fixed offsets and every other byte is rewritten by a call before
+ * the call reads it.  Calls that may run concurrently (different streams)
+ * need different workspaces.
+ *
+ * Compensated layers need a workspace for every call.  For a layer with
+ * r == 0 it is optional: decode never uses it, and prefill uses it to split
+ * K across workgroups when the output has few 128 x 128 tiles (small M).
  */
 size_t spear_workspace_bytes(const spear_layer_t *layer, int32_t M);
 

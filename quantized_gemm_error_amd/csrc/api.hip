@@ -155,7 +155,9 @@ spear_status_t spear_linear_prefill(const spear_layer_t *layer, spear_dtype_t dt
   if (M == 0) return ok();
   if (M > (1 << 24)) return fail(SPEAR_ERR_UNSUPPORTED, "prefill M=%d too large", M);
   if ((st = check_io(dtype, x, y)) != SPEAR_OK) return st;
-  if ((st = check_ws(workspace, workspace_bytes, prefill_workspace_bytes(d, M))) != SPEAR_OK)
+  // a rank-0 layer may come without a workspace (then K is never split)
+  if ((workspace || prefill_needs_workspace(d)) &&
+      (st = check_ws(workspace, workspace_bytes, prefill_workspace_bytes(d, M))) != SPEAR_OK)
     return st;
   return hip_status(launch_prefill(d, (int)dtype, (const uint16_t *)x, (uint16_t *)y, M, workspace,
                                    (hipStream_t)main_stream, (hipStream_t)aux_stream),

@@ -723,7 +723,7 @@ size_t decode_workspace_bytes(const LayerDesc &L, int M) {
   if (L.rank == 0) return 0;
   const DecodePlan p = plan_decode(L, M);
   if (!p.ok) return 0;
-  return sizeof(WsHeader) + (size_t)p.producers * 16 * (16 * p.mb) * sizeof(float);
+  return kWsDataOff + (size_t)p.producers * 16 * (16 * p.mb) * sizeof(float);
 }
 
 hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
@@ -762,7 +762,7 @@ hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint1
   a.ks = p.ks;
   a.part_bytes = (int)((size_t)p.producers * 16 * (16 * p.mb) * sizeof(float));
   a.hdr = (WsHeader *)ws;
-  a.part = ws ? (float *)((char *)ws + sizeof(WsHeader)) : nullptr;
+  a.part = ws ? (float *)((char *)ws + kWsDataOff) : nullptr;
   const bool ec = L.rank > 0;
   return dtype == DT_F16 ? launch_mb<DT_F16>(a, p, ec, L.per_channel, s)
                          : launch_mb<DT_BF16>(a, p, ec, L.per_channel, s);

@@ -27,6 +27,12 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) == 2048, "workspace header is 2048 bytes");
 
+// The header holds every counter a call relies on finding at zero; from
+// kWsDataOff on, every byte a call reads it has written itself first, so one
+// workspace may serve several layers.
+constexpr size_t kWsDataOff = sizeof(WsHeader);
+static_assert(kWsDataOff % 256 == 0, "data region 256-byte aligned");
+
 
 // Everything a launcher needs, already validated.
 struct LayerDesc {
@@ -62,6 +68,7 @@ DecodePlan plan_decode(const LayerDesc &L, int M);
 bool decode_supported(const LayerDesc &L, int M);
 size_t decode_workspace_bytes(const LayerDesc &L, int M);
 size_t prefill_workspace_bytes(const LayerDesc &L, int M);
+bool prefill_needs_workspace(const LayerDesc &L);  // false: optional (splits K when given)
 
 hipError_t launch_pack_int4(const uint8_t *q, int32_t *out, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,

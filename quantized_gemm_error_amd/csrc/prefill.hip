@@ -5,23 +5,34 @@
 // kernel that overlaps the low-bit GEMM instead of fusing it (SPEAR
 // explanation page, Technical Summary 2.2 A, prefill phase).  Here:
 //
-//  * prefill_ec_kernel computes U = diag(g) (X A^T), g = sigmoid(X w_g + b_g),
-//    into the workspace (fp32).  K is split over several workgroups per 16
-//    tokens; the last split to finish sums the partials in a fixed order;
+//  * prefill_ec_kernel computes the sums [A; w_g] x per token (rows 0..rank,
+//    the last being the gate's pre-activation z) into the workspace, with K
+//    split over up to four workgroups per 32 tokens; each split stores its
+//    own partial sums;
 //  * prefill_gemm_kernel, a 128x128x128-tiled MFMA GEMM.  Each k-block stages
 //    the activation tile and the exactly dequantized weight tile (q - z in
 //    the activation type) in LDS; four waves each own a 64x64 quarter of the
 //    output tile and run 16x16x32 MFMAs, applying each row's fp32 scale once
 //    per 128-wide block (or once at the end when one scale covers the row).
+//    When the output has too few tiles to fill the chip, K is split over
+//    several workgroups that store fp32 partial tiles;
+//  * prefill_finish_kernel completes 64x64 output tiles: the sum of the GEMM's
+//    split partials (with the per-channel scale) or the rounded y of the
+//    concurrent schedule, plus U B^T, rounded once into y.
 //
-// Two schedules:
-//  * serial (no aux stream): the EC kernel, then the GEMM, whose epilogue adds
-//    U B^T with fp32 16x16x4 MFMAs before y is rounded once.  On MI355X this
-//    is the faster order: the GEMM's workgroups fill every CU, so a kernel on
-//    another stream only runs as they retire;
-//  * concurrent (aux stream given, the pages' schedule): the EC kernel on the
-//    aux stream alongside the GEMM on the main stream, then, after joining,
-//    prefill_merge_kernel adds U B^T to the rounded y.
+// Whoever needs U = diag(g) (X A^T) forms it from the compensator's split
+// partials, summed in split order: g = sigmoid(z + b_g).  Every reduction
+// across workgroups happens across a kernel boundary, so no kernel here
+// waits on another workgroup.
+//
+// Schedules:
+//  * serial (no aux stream): compensator, then the GEMM, whose epilogue adds
+//    U B^T before y is rounded once (or, with K split, the finish kernel
+//    does).  On MI355X this is the faster order: the GEMM's workgroups fill
+//    every CU, so a kernel on another stream only runs as they retire;
+//  * concurrent (aux stream given, the pages' schedule): the compensator on
+//    the aux stream alongside the GEMM on the main stream; after the join the
+//    finish kernel adds U B^T.
 #include <mutex>
 #include <unordered_map>
 
@@ -35,15 +46,38 @@ namespace {
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int LSTR = BK + 8;  // LDS row stride (halves), padded against bank conflicts
 
+// The compensator's split partials: Tp[q][m][j], j = 0..rank (j = rank: z).
+struct EcView {
+  const float *Tp;
+  int ks, M, rank, rp1;
+  float b_gate;
+};
+
+// Sum of token m's split partials of row j, in split order.
+__device__ __forceinline__ float ec_sum(const EcView &e, int m, int j) {
+  float t = 0.f;
+  for (int q = 0; q < e.ks; ++q) t += e.Tp[((size_t)q * e.M + m) * e.rp1 + j];
+  return t;
+}
+
+// Four consecutive rows j..j+3 of token m (rp1 is a multiple of 4, so the
+// four values are one 16-byte piece of each split's row).
+__device__ __forceinline__ f32x4_t ec_sum4(const EcView &e, int m, int j) {
+  f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < e.ks; ++q) t += *(const f32x4_t *)(e.Tp + ((size_t)q * e.M + m) * e.rp1 + j);
+  return t;
+}
+
 struct GemmArgs {
   const uint32_t *qw;
   const uint16_t *scales, *zeros;
   const uint16_t *x;
   uint16_t *y;
   int N, K, G, ngroups, M;
-  const float *U;     // EPI: [M][rp] gated compensator input, ready before the launch
+  EcView ec;          // EPI: the compensator's partials, complete before the launch
   const uint16_t *B;  // EPI: [N][rank]
-  int rank, rp;
+  int ks;             // SPLIT: K splits (blockIdx.z), each a contiguous range of k-blocks
+  float *part;        // SPLIT: [ks][M][N] fp32 partial outputs
 };
 
 constexpr int kEpiRc = 32;           // ranks per epilogue chunk
@@ -51,11 +85,13 @@ constexpr int kEpiStr = kEpiRc + 4;  // LDS row stride of the chunk (floats)
 static_assert(BM * kEpiStr * 4 <= BM * LSTR * 2, "epilogue U chunk fits the activation tile");
 static_assert(BN * kEpiStr * 4 <= BN * LSTR * 2, "epilogue B chunk fits the weight tile");
 
-template <int DT, bool PERCH, bool EPI>
+template <int DT, bool PERCH, bool EPI, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
+  static_assert(!(EPI && SPLIT), "split tiles are finished by prefill_finish_kernel");
   __shared__ __align__(16) uint16_t xs[BM * LSTR];
   __shared__ __align__(16) uint16_t wsm[BN * LSTR];
   __shared__ float ss[BN];
+  __shared__ float gs[BM];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, h = lane >> 4;
@@ -78,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
       xr[i] = (m < a.M && k < a.K) ? *(const u32x4_t *)(a.x + (size_t)m * a.K + k)
                                    : u32x4_t{0u, 0u, 0u, 0u};
     }
-    const int g = PERCH ? 0 : (kb * BK) / a.G;
+    const int g = PERCH ? 0 : min((kb * BK) / a.G, a.ngroups - 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int p = tid + 256 * i;
@@ -117,12 +153,19 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  for (int kb = 0; kb < nkb; ++kb) {
+  // this workgroup's k-blocks: all of them, or split blockIdx.z of ks
+  int kb_lo = 0, kb_hi = nkb;
+  if constexpr (SPLIT) {
+    const int per = (nkb + a.ks - 1) / a.ks;
+    kb_lo = min(nkb, (int)blockIdx.z * per);
+    kb_hi = min(nkb, kb_lo + per);
+  }
+  if (kb_lo < kb_hi) gload(kb_lo);
+  for (int kb = kb_lo; kb < kb_hi; ++kb) {
     __syncthreads();
     lstore();
     __syncthreads();
-    if (kb + 1 < nkb) gload(kb + 1);
+    if (kb + 1 < kb_hi) gload(kb + 1);
 
     u32x4_t af[4][4];
 #pragma unroll
@@ -155,6 +198,23 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
     }
   }
 
+  if constexpr (SPLIT) {
+    // this split's fp32 partial tile; the finish kernel sums the splits
+    float *P = a.part + (size_t)blockIdx.z * a.M * a.N;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int n = n0 + 64 * wn + 16 * ni + col;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + 64 * wm + 16 * mi + 4 * h + e;
+          if (m < a.M && n < a.N) P[(size_t)m * a.N + n] = acc[mi][ni][e];
+        }
+    }
+    return;
+  }
+
   if constexpr (PERCH) {
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
@@ -166,44 +226,35 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
   }
 
   if constexpr (EPI) {
-    // y tile += U[m0.., :] B[n0.., :]^T, kEpiRc ranks at a time staged in the
-    // (now free) LDS tiles; rows past M or N and ranks past r stage zeros
+    // y tile += U[m0.., :] B[n0.., :]^T with U = g * T formed from the
+    // compensator's split partials; kEpiRc ranks at a time staged in the (now
+    // free) LDS tiles; rows past M or N and ranks past r stage zeros
+    const EcView &e = a.ec;
+    __syncthreads();  // the tiles' last readers are done
+    if (tid < BM) gs[tid] = (m0 + tid < a.M) ? gate_sigmoid(ec_sum(e, m0 + tid, e.rank) + e.b_gate) : 0.f;
     float *us = (float *)xs;
     float *bs = (float *)wsm;
     const int uq = kEpiRc / 4;
-    for (int j0 = 0; j0 < a.rank; j0 += kEpiRc) {
-      f32x4_t uv[4];
+    for (int j0 = 0; j0 < e.rank; j0 += kEpiRc) {
+      __syncthreads();  // gs written / the previous chunk's readers are done
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int p = tid + 256 * i;  // BM rows x uq pieces
         const int r = p / uq, q = p - r * uq;
         const int j = j0 + 4 * q;
-        uv[i] = (m0 + r < a.M && j < a.rp) ? *(const f32x4_t *)(a.U + (size_t)(m0 + r) * a.rp + j)
-                                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+        if (m0 + r < a.M && j < e.rp1) u = gs[r] * ec_sum4(e, m0 + r, j);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (j + e >= a.rank) uv[i][e] = 0.f;
+        for (int c = 0; c < 4; ++c)
+          if (j + c >= e.rank) u[c] = 0.f;
+        *(f32x4_t *)(us + r * kEpiStr + 4 * q) = u;
       }
-      uint16_t bv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int p = tid + 256 * i;  // BN rows x kEpiRc ranks
         const int r = p / kEpiRc, jj = p - r * kEpiRc;
-        bv[i] = (n0 + r < a.N && j0 + jj < a.rank) ? a.B[(size_t)(n0 + r) * a.rank + j0 + jj]
-                                                  : (uint16_t)0;
-      }
-      __syncthreads();  // the tiles' last readers are done
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = tid + 256 * i;
-        const int r = p / uq, q = p - r * uq;
-        *(f32x4_t *)(us + r * kEpiStr + 4 * q) = uv[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int p = tid + 256 * i;
-        const int r = p / kEpiRc, jj = p - r * kEpiRc;
-        bs[r * kEpiStr + jj] = to_f32<DT>(bv[i]);
+        bs[r * kEpiStr + jj] = (n0 + r < a.N && j0 + jj < e.rank)
+                                   ? to_f32<DT>(a.B[(size_t)(n0 + r) * e.rank + j0 + jj]) : 0.f;
       }
       __syncthreads();
 #pragma unroll
@@ -237,26 +288,19 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Compensator: U[m][j] = g[m] * sum_k A[j][k] x[m][k], g[m] = sigmoid(z[m] + b_g),
-// z[m] = sum_k w_g[k] x[m][k].
+// Compensator sums: Tp[ksi][m][j] = sum over split ksi's K range of
+// [A; w_g][j][k] x[m][k], j = 0..rank.
 //
 // Workgroup (blk, ksi) takes kEcTok = 32 tokens (two MFMA row blocks) and K
 // split ksi of ks; its eight waves take interleaved 32-wide K steps.  Up to
 // kEcRb 16-row blocks of [A; w_g] are accumulated together, so each weight
 // piece feeds both token blocks and each activation piece feeds kEcRb MFMAs;
-// each wave keeps kEcU steps of loads in flight before it multiplies.  Wave 0
-// publishes the split's sums (rows 0..rank, the last being z) with
-// agent-scope atomic stores, a release and a per-block counter; the split
-// that completes the count sums the ks partials in split order, applies the
-// gate, writes U and resets the counter for the next call.
+// each wave keeps kEcU steps of loads in flight before it multiplies.
 // ---------------------------------------------------------------------------
 struct EcArgs {
   const uint16_t *x, *A, *wg;
-  float b_gate;
-  int K, M, rank, rp, rp1, ks;
-  float *U;        // [M][rp]
-  float *Tp;       // [ks][M][rp1]: partial sums of [A; w_g] x per split
-  uint32_t *cnt;   // [ceil(M / kEcTok)] splits finished per token block
+  int K, M, rank, rp1, ks;
+  float *Tp;  // [ks][M][rp1]
 };
 
 constexpr int kEcWaves = 8, kEcRb = 3, kEcU = 4, kEcTok = 32, kEcMb = kEcTok / 16;
@@ -268,7 +312,6 @@ template <int DT>
 __global__ __launch_bounds__(64 * kEcWaves) void prefill_ec_kernel(EcArgs a) {
   __shared__ f32x4_t red[kEcWaves][kEcRb][kEcMb][64];
   __shared__ float tz[kEcTok][kTzStride];
-  __shared__ uint32_t last;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, h = lane >> 4;
   const int blk = blockIdx.x / a.ks, ksi = blockIdx.x % a.ks;
@@ -348,196 +391,168 @@ __global__ __launch_bounds__(64 * kEcWaves) void prefill_ec_kernel(EcArgs a) {
     __syncthreads();
   }
 
-  const int nval = kEcTok * (a.rank + 1);  // this block's values: its tokens x rows 0..rank
-  if (wave == 0) {
-    uint32_t *tp = (uint32_t *)a.Tp + ((size_t)ksi * a.M + m0) * a.rp1;
-    for (int i = lane; i < nval; i += 64) {
-      const int mm = i / (a.rank + 1), j = i - mm * (a.rank + 1);
-      if (m0 + mm < a.M)
-        __hip_atomic_store(&tp[(size_t)mm * a.rp1 + j], bitcast<uint32_t>(tz[mm][j]),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if (lane == 0)
-      last = __hip_atomic_fetch_add(&a.cnt[blk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (uint32_t)(a.ks - 1);
-  }
-  __syncthreads();
-  if (!last) return;
-  // the last split: every partial of this block has been published
+
+  // this split's sums, rows 0..rank of its tokens
+  const int nval = kEcTok * (a.rank + 1);
+  float *tp = a.Tp + ((size_t)ksi * a.M + m0) * a.rp1;
   for (int i = tid; i < nval; i += 64 * kEcWaves) {
     const int mm = i / (a.rank + 1), j = i - mm * (a.rank + 1);
-    float t = 0.f;
-    if (m0 + mm < a.M) {
-      for (int q = 0; q < a.ks; ++q)
-        t += bitcast<float>(__hip_atomic_load(
-            (const uint32_t *)a.Tp + ((size_t)q * a.M + m0 + mm) * a.rp1 + j, __ATOMIC_RELAXED,
-            __HIP_MEMORY_SCOPE_AGENT));
-    }
-    tz[mm][j] = t;
+    if (m0 + mm < a.M) tp[(size_t)mm * a.rp1 + j] = tz[mm][j];
   }
-  __syncthreads();
-  for (int i = tid; i < kEcTok * a.rank; i += 64 * kEcWaves) {
-    const int mm = i / a.rank, j = i - mm * a.rank;
-    const int m = m0 + mm;
-    if (m < a.M) {
-      const float g = gate_sigmoid(tz[mm][a.rank] + a.b_gate);
-      a.U[(size_t)m * a.rp + j] = g * tz[mm][j];
-    }
-  }
-  if (tid == 0) __hip_atomic_store(&a.cnt[blk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---------------------------------------------------------------------------
-// Merge on the main stream after the join: y[m][n] += sum_j U[m][j] B[n][j]
-// for a 64-token x 64-output tile.  The y tile, the 64 U rows and the 64 B
-// rows are staged in LDS (loads issued together, 16 bytes where the layout
-// allows), four waves each take 16 tokens with fp32 16x16x4 MFMAs, and y
-// goes back in 16-byte stores when its rows are 16-byte aligned.
-// ---------------------------------------------------------------------------
-struct MergeArgs {
-  uint16_t *y;
-  const uint16_t *B;
-  const float *U;  // [M][rp]
-  int N, M, rank, rp;
+// Sum of the compensator's split partials, Ts[m][j] = sum_q Tp[q][m][j] in
+// split order, for the many-split case (few tokens): consumers then read one
+// partial per value.
+struct EcSumArgs {
+  const float *Tp;
+  float *Ts;  // [M][rp1]
+  int ks, M, rank, rp1;
 };
 
-constexpr int kMgT = 64;              // tokens and outputs per tile
-constexpr int kMgYStr = kMgT + 8;     // LDS row stride of the y tile (halves)
-
-__host__ __device__ constexpr int merge_rstr(int rp) { return rp + 4; }  // floats; 16-byte rows
-__host__ __device__ constexpr size_t merge_lds_bytes(int rp) {
-  return (size_t)2 * kMgT * merge_rstr(rp) * 4 + (size_t)kMgT * kMgYStr * 2;
+__global__ __launch_bounds__(256) void prefill_ec_sum_kernel(EcSumArgs a) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int n = a.M * (a.rank + 1);
+  if (i >= n) return;
+  const int m = i / (a.rank + 1), j = i - m * (a.rank + 1);
+  float t = 0.f;
+  for (int q = 0; q < a.ks; ++q) t += a.Tp[((size_t)q * a.M + m) * a.rp1 + j];
+  a.Ts[(size_t)m * a.rp1 + j] = t;
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(MergeArgs a) {
-  extern __shared__ __align__(16) float mlds[];
-  const int rstr = merge_rstr(a.rp);
-  float *us = mlds;                                    // [64][rstr]
-  float *bs = us + kMgT * rstr;                        // [64][rstr]
-  uint16_t *ys = (uint16_t *)(bs + kMgT * rstr);       // [64][kMgYStr]
+// ---------------------------------------------------------------------------
+// Finish a 64-token x 64-output tile:
+//   y[m][n] = round( base[m][n] + sum_j U[m][j] B[n][j] )
+// where base is the sum of the GEMM's split partials in split order (times
+// the row's scale when one scale covers the row) or, in the concurrent
+// schedule, the GEMM's rounded y; the U B^T term is present when the layer
+// has a compensator.  The base tile, the U rows (formed from the
+// compensator's partials) and the B rows are staged in LDS; four waves each
+// take 16 tokens with fp32 16x16x4 MFMAs; y goes back in 16-byte stores when
+// its rows are 16-byte aligned.
+// ---------------------------------------------------------------------------
+struct FinishArgs {
+  uint16_t *y;
+  const float *part;  // PARTS: [ks][M][N]
+  int ks;
+  const uint16_t *scales;  // PARTS && PERCH: [N]
+  EcView ec;               // EC
+  const uint16_t *B;       // EC: [N][rank]
+  int N, M;
+};
+
+constexpr int kFT = 64;              // tokens and outputs per tile
+constexpr int kFStr = kFT + 4;       // fp32 base tile row stride
+constexpr int kFRc = 32;             // ranks per chunk
+constexpr int kFRStr = kFRc + 4;
+
+template <int DT, bool PARTS, bool PERCH, bool EC>
+__global__ __launch_bounds__(256) void prefill_finish_kernel(FinishArgs a) {
+  __shared__ __align__(16) float ts[kFT][kFStr];
+  __shared__ __align__(16) float us[kFT][kFRStr];
+  __shared__ __align__(16) float bs[kFT][kFRStr];
+  __shared__ float gs[kFT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, h = lane >> 4;
-  const int n0 = blockIdx.x * kMgT, m0 = blockIdx.y * kMgT;
-  const bool yvec = (a.N % 8) == 0;
+  const int n0 = blockIdx.x * kFT, m0 = blockIdx.y * kFT;
 
-  // --- stage: y tile (8 halves per piece), U rows (4 floats), B rows (scalars)
-  u32x4_t yv[2];
+  // --- base tile: 64 rows x 16 pieces of 4
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = tid + 256 * i;  // 512 pieces of 8 halves
-    const int r = p >> 3, c8 = (p & 7) * 8;
-    const int m = m0 + r, n = n0 + c8;
-    yv[i] = u32x4_t{0u, 0u, 0u, 0u};
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + 256 * i;
+    const int r = p >> 4, c4 = (p & 15) * 4;
+    const int m = m0 + r, n = n0 + c4;
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
     if (m < a.M) {
-      if (yvec && n + 8 <= a.N) {
-        yv[i] = *(const u32x4_t *)(a.y + (size_t)m * a.N + n);
-      } else {
-        uint16_t t[8];
+      if constexpr (PARTS) {
+        const bool vec = (a.N % 4) == 0 && n + 4 <= a.N;
+        for (int q = 0; q < a.ks; ++q) {
+          const float *src = a.part + ((size_t)q * a.M + m) * a.N + n;
+          if (vec) {
+            v += *(const f32x4_t *)src;
+          } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = (n + e < a.N) ? a.y[(size_t)m * a.N + n + e] : 0;
-        yv[i] = bitcast<u32x4_t>(t);
+            for (int c = 0; c < 4; ++c)
+              if (n + c < a.N) v[c] += src[c];
+          }
+        }
+        if constexpr (PERCH) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            v[c] *= (n + c < a.N) ? (float)bitcast<_Float16>(a.scales[n + c]) : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          v[c] = (n + c < a.N) ? to_f32<DT>(a.y[(size_t)m * a.N + n + c]) : 0.f;
+      }
+    }
+    *(f32x4_t *)&ts[r][c4] = v;
+  }
+
+  if constexpr (EC) {
+    const EcView &e = a.ec;
+    if (tid < kFT) gs[tid] = (m0 + tid < a.M) ? gate_sigmoid(ec_sum(e, m0 + tid, e.rank) + e.b_gate) : 0.f;
+    for (int j0 = 0; j0 < e.rank; j0 += kFRc) {
+      __syncthreads();  // gs / base tile written; the previous chunk's readers are done
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int p = tid + 256 * i;  // 64 rows x 8 pieces
+        const int r = p >> 3, q = p & 7;
+        const int j = j0 + 4 * q;
+        f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+        if (m0 + r < a.M && j < e.rp1) u = gs[r] * ec_sum4(e, m0 + r, j);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (j + c >= e.rank) u[c] = 0.f;
+        *(f32x4_t *)&us[r][4 * q] = u;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int p = tid + 256 * i;  // 64 rows x 32 ranks
+        const int r = p >> 5, jj = p & 31;
+        bs[r][jj] = (n0 + r < a.N && j0 + jj < e.rank)
+                        ? to_f32<DT>(a.B[(size_t)(n0 + r) * e.rank + j0 + jj]) : 0.f;
+      }
+      __syncthreads();
+      const int tk = 16 * wave + col;  // A-operand row (token) of this lane
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        f32x4_t acc;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = ts[16 * wave + 4 * h + c][16 * nb + col];
+#pragma unroll
+        for (int st = 0; st < kFRc / 4; ++st) {
+          const int j = 4 * st + h;
+          acc = mfma_16x16x4_f32(us[tk][j], bs[16 * nb + col][j], acc);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ts[16 * wave + 4 * h + c][16 * nb + col] = acc[c];
       }
     }
   }
-  const int uq = a.rp / 4;  // 16-byte pieces per U row
-  for (int p0 = 0; p0 < kMgT * uq; p0 += 256 * 4) {
-    f32x4_t uv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = p0 + tid + 256 * i;
-      const int r = p / uq, q = p - r * uq;
-      uv[i] = (p < kMgT * uq && m0 + r < a.M)
-                  ? *(const f32x4_t *)(a.U + (size_t)(m0 + r) * a.rp + 4 * q)
-                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = p0 + tid + 256 * i;
-      const int r = p / uq, q = p - r * uq;
-      // columns rank .. rp-1 of U are never written: zero them, whatever the
-      // workspace held there
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * q + e >= a.rank) uv[i][e] = 0.f;
-      if (p < kMgT * uq) *(f32x4_t *)(us + r * rstr + 4 * q) = uv[i];
-    }
-  }
-  for (int p0 = 0; p0 < kMgT * a.rp; p0 += 256 * 8) {
-    uint16_t bv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = p0 + tid + 256 * i;
-      const int r = p / a.rp, j = p - r * a.rp;
-      bv[i] = (p < kMgT * a.rp && n0 + r < a.N && j < a.rank)
-                  ? a.B[(size_t)(n0 + r) * a.rank + j] : (uint16_t)0;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = p0 + tid + 256 * i;
-      const int r = p / a.rp, j = p - r * a.rp;
-      if (p < kMgT * a.rp) bs[r * rstr + j] = to_f32<DT>(bv[i]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = tid + 256 * i;
-    const int r = p >> 3, c8 = (p & 7) * 8;
-    *(u32x4_t *)(ys + r * kMgYStr + c8) = yv[i];
-  }
   __syncthreads();
 
-  // --- multiply: wave takes tokens 16 wave .. +16, all 64 outputs
-  const int nst = a.rp / 4;
-  const int tk = 16 * wave + col;  // A-operand row (token) of this lane
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    f32x4_t acc;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = to_f32<DT>(ys[(16 * wave + 4 * h + e) * kMgYStr + 16 * nb + col]);
-    for (int st = 0; st < nst; ++st) {
-      const int j = 4 * st + h;
-      acc = mfma_16x16x4_f32(us[tk * rstr + j], bs[(16 * nb + col) * rstr + j], acc);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ys[(16 * wave + 4 * h + e) * kMgYStr + 16 * nb + col] = from_f32<DT>(acc[e]);
-  }
-  __syncthreads();
-
-  // --- store the tile
+  // --- round and store: 64 rows x 8 pieces of 8
+  const bool yvec = (a.N % 8) == 0 && ((uintptr_t)a.y % 16) == 0;  // y itself need only be 2-byte aligned
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = tid + 256 * i;
     const int r = p >> 3, c8 = (p & 7) * 8;
     const int m = m0 + r, n = n0 + c8;
     if (m < a.M) {
-      const u32x4_t v = *(const u32x4_t *)(ys + r * kMgYStr + c8);
-      if (yvec && n + 8 <= a.N) {
-        *(u32x4_t *)(a.y + (size_t)m * a.N + n) = v;
-      } else {
-        const u16x8_t t = bitcast<u16x8_t>(v);
+      u16x8_t t;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (n + e < a.N) a.y[(size_t)m * a.N + n + e] = t[e];
+      for (int c = 0; c < 8; ++c) t[c] = from_f32<DT>(ts[r][c8 + c]);
+      if (yvec && n + 8 <= a.N) {
+        *(u16x8_t *)(a.y + (size_t)m * a.N + n) = t;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (n + c < a.N) a.y[(size_t)m * a.N + n + c] = t[c];
       }
     }
   }
-}
-
-// Merge launch; the dynamic LDS can exceed the 64 KB default (rank 128: 78 KB).
-template <int DT>
-hipError_t launch_merge(const MergeArgs &ma, dim3 grid, size_t lds, hipStream_t s) {
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute((const void *)prefill_merge_kernel<DT>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)merge_lds_bytes((SPEAR_MAX_RANK + 3) / 4 * 4));
-  });
-  if (attr_err != hipSuccess) return attr_err;
-  hipLaunchKernelGGL(prefill_merge_kernel<DT>, grid, dim3(256), lds, s, ma);
-  return hipGetLastError();
 }
 
 struct StreamEvents {
@@ -566,79 +581,111 @@ hipError_t get_events(StreamEvents **out) {
 static int rank_pad(int rank) { return (rank + 3) / 4 * 4; }
 static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Compensator K-splits: enough workgroups (about 512) to keep the activation
-// stream busy, at most 16, and at least one 32-wide step per wave per split.
-constexpr int kEcMaxKs = 16;
+// Compensator K splits: about 256 workgroups of 32 tokens, at least one
+// 32-wide step per wave, at most 64.  Up to kEcDirectKs splits the consumers
+// of U sum them directly; beyond that prefill_ec_sum_kernel sums them once.
+// ks * ceil(M / 32) <= 256 + ceil(M / 32) bounds the partials.
+constexpr int kEcDirectKs = 4;
 static int ec_ksplit(int M, int K) {
   const int nblk = (M + kEcTok - 1) / kEcTok;
   int ks = (256 + nblk - 1) / nblk;
-  if (ks > 4) ks = 4;  // each extra split adds a publish and a gather
+  if (ks > 64) ks = 64;
   const int cap = (K / 32) / kEcWaves;
   if (ks > cap) ks = cap;
-  if (ks > kEcMaxKs) ks = kEcMaxKs;
   return ks < 1 ? 1 : ks;
 }
 
-// Workspace after the 2048-byte header: split counters [ceil(M/32)], U
-// [M][rp] and the split partials [ks][M][rp1], each 256-byte aligned.  The
-// counters must start at zero, so they sit past the largest region a decode
-// call writes (its partial sums follow the header); U and the partials are
-// rewritten in full by every call and may share bytes with decode's.
+// GEMM K splits: when the output has too few 128x128 tiles to fill the chip,
+// split K so that about kGemmSplitWgs workgroups run, each with at least 4
+// k-blocks and none empty.  ks * tiles <= kGemmSplitWgs bounds the partials.
+constexpr int kGemmSplitWgs = 512;
+static int gemm_ksplit(int M, int N, int K) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int nkb = (K + BK - 1) / BK;
+  if (tiles >= kGemmSplitWgs * 3 / 4) return 1;
+  int ks = kGemmSplitWgs / tiles;
+  if (ks > nkb / 4) ks = nkb / 4;
+  if (ks > 16) ks = 16;
+  if (ks < 2) return 1;
+  const int per = (nkb + ks - 1) / ks;
+  return (nkb + per - 1) / per;  // no empty split
+}
+
+// Workspace layout after the 2048-byte header: the compensator's split
+// partials [ks][M][rp1], their sum [M][rp1] (many splits only) and the GEMM's
+// split partials (at most kGemmSplitWgs tiles of 128 x 128 fp32).  All are
+// rewritten in full by every call before they are read and are sized by
+// bounds that grow with M, so a workspace for M serves every call with fewer
+// tokens, and any other layer whose size it covers.
 struct PrefillWs {
-  size_t cnt_off, u_off, tp_off, end;
+  size_t tp, ts, gpart, end;
 };
 static PrefillWs prefill_ws_layout(const LayerDesc &L, int M) {
   PrefillWs w;
-  const int nblk = (M + kEcTok - 1) / kEcTok;
-  size_t dec = 0;  // decode's bytes for one (M <= 16) and two (M <= 32) token blocks
-  for (int dm : {16, SPEAR_MAX_DECODE_M}) {
-    const size_t b = decode_workspace_bytes(L, dm);
-    if (b > dec) dec = b;
-  }
-  w.cnt_off = dec > sizeof(WsHeader) ? round256(dec) : sizeof(WsHeader);
-  w.u_off = w.cnt_off + round256((size_t)nblk * sizeof(uint32_t));
-  w.tp_off = w.u_off + round256((size_t)M * rank_pad(L.rank) * sizeof(float));
-  // sized for the most splits, so that a workspace for M serves every call
-  // with fewer tokens too (the split count is not monotone in M)
-  w.end = w.tp_off + round256((size_t)kEcMaxKs * M * rank_pad(L.rank + 1) * sizeof(float));
+  w.tp = kWsDataOff;
+  const size_t rp1 = rank_pad(L.rank + 1);
+  const size_t nblk = (M + kEcTok - 1) / kEcTok;
+  const size_t tb = L.rank > 0 ? round256((256 + nblk) * kEcTok * rp1 * sizeof(float)) : 0;
+  const size_t sb = L.rank > 0 ? round256((size_t)M * rp1 * sizeof(float)) : 0;
+  w.ts = w.tp + tb;
+  w.gpart = w.ts + sb;
+  w.end = w.gpart + (size_t)kGemmSplitWgs * BM * BN * sizeof(float);
   return w;
 }
 
-size_t prefill_workspace_bytes(const LayerDesc &L, int M) {
-  if (L.rank == 0) return 0;
-  return prefill_ws_layout(L, M).end;
-}
+size_t prefill_workspace_bytes(const LayerDesc &L, int M) { return prefill_ws_layout(L, M).end; }
 
-template <int DT, bool PERCH, bool EPI>
-static void launch_gemm(const GemmArgs &g, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_gemm_kernel<DT, PERCH, EPI>), grid, dim3(256), 0, s, g);
-}
+bool prefill_needs_workspace(const LayerDesc &L) { return L.rank > 0; }
 
-template <int DT>
-static void launch_gemm_dt(const GemmArgs &g, dim3 grid, bool perch, bool epi, hipStream_t s) {
-  if (perch)
-    epi ? launch_gemm<DT, true, true>(g, grid, s) : launch_gemm<DT, true, false>(g, grid, s);
+template <int DT, bool PERCH>
+static void launch_gemm(const GemmArgs &g, dim3 grid, bool epi, hipStream_t s) {
+  if (grid.z > 1)
+    hipLaunchKernelGGL((prefill_gemm_kernel<DT, PERCH, false, true>), grid, dim3(256), 0, s, g);
+  else if (epi)
+    hipLaunchKernelGGL((prefill_gemm_kernel<DT, PERCH, true, false>), grid, dim3(256), 0, s, g);
   else
-    epi ? launch_gemm<DT, false, true>(g, grid, s) : launch_gemm<DT, false, false>(g, grid, s);
+    hipLaunchKernelGGL((prefill_gemm_kernel<DT, PERCH, false, false>), grid, dim3(256), 0, s, g);
+}
+
+template <int DT, bool PARTS>
+static void launch_finish(const FinishArgs &f, dim3 grid, bool perch, bool ec, hipStream_t s) {
+  if (perch && ec)
+    hipLaunchKernelGGL((prefill_finish_kernel<DT, PARTS, true, true>), grid, dim3(256), 0, s, f);
+  else if (perch)
+    hipLaunchKernelGGL((prefill_finish_kernel<DT, PARTS, true, false>), grid, dim3(256), 0, s, f);
+  else if (ec)
+    hipLaunchKernelGGL((prefill_finish_kernel<DT, PARTS, false, true>), grid, dim3(256), 0, s, f);
+  else
+    hipLaunchKernelGGL((prefill_finish_kernel<DT, PARTS, false, false>), grid, dim3(256), 0, s, f);
 }
 
 hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
                           void *ws, hipStream_t main_s, hipStream_t aux_s) {
   const bool ec = L.rank > 0;
   const bool concurrent = ec && aux_s != nullptr && aux_s != main_s;
-  const int rp = rank_pad(L.rank);
-  float *U = nullptr;
+  const PrefillWs w = prefill_ws_layout(L, M);
+  char *base = (char *)ws;
+  EcView ev{};
   EcArgs ea{};
+  int eks = 1;
   if (ec) {
-    const PrefillWs w = prefill_ws_layout(L, M);
-    char *base = (char *)ws;
-    U = (float *)(base + w.u_off);
-    ea = EcArgs{x, L.A, L.wg, L.b_gate, L.K, M, L.rank, rp, rank_pad(L.rank + 1), ec_ksplit(M, L.K),
-                U, (float *)(base + w.tp_off), (uint32_t *)(base + w.cnt_off)};
+    const int rp1 = rank_pad(L.rank + 1);
+    eks = ec_ksplit(M, L.K);
+    ea = EcArgs{x, L.A, L.wg, L.K, M, L.rank, rp1, eks, (float *)(base + w.tp)};
+    // consumers read the split partials directly, or their one-time sum
+    ev = eks <= kEcDirectKs
+             ? EcView{(const float *)(base + w.tp), eks, M, L.rank, rp1, L.b_gate}
+             : EcView{(const float *)(base + w.ts), 1, M, L.rank, rp1, L.b_gate};
   }
-  GemmArgs g{L.qw, L.scales, L.zeros, x, y, L.N, L.K, L.G, L.ngroups, M, U, L.B, L.rank, rp};
-  const dim3 ggrid((L.N + BN - 1) / BN, (M + BM - 1) / BM);
-  const dim3 egrid(((M + kEcTok - 1) / kEcTok) * (ec ? ea.ks : 1));
+  // split K only with a workspace (a rank-0 call may come without one)
+  const int gks = ws ? gemm_ksplit(M, L.N, L.K) : 1;
+  const bool split = gks > 1;
+  GemmArgs g{L.qw, L.scales, L.zeros, x, y, L.N, L.K, L.G, L.ngroups, M, ev, L.B, gks,
+             split ? (float *)(base + w.gpart) : nullptr};
+  const dim3 ggrid((L.N + BN - 1) / BN, (M + BM - 1) / BM, gks);
+  const dim3 egrid(((M + kEcTok - 1) / kEcTok) * eks);
+  const dim3 fgrid((L.N + kFT - 1) / kFT, (M + kFT - 1) / kFT);
+  FinishArgs fa{y, g.part, gks, L.scales, ev, L.B, L.N, M};
   hipError_t e = hipSuccess;
 
   auto launch_ec = [&](hipStream_t s) {
@@ -646,38 +693,68 @@ hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint
       hipLaunchKernelGGL(prefill_ec_kernel<DT_F16>, egrid, dim3(64 * kEcWaves), 0, s, ea);
     else
       hipLaunchKernelGGL(prefill_ec_kernel<DT_BF16>, egrid, dim3(64 * kEcWaves), 0, s, ea);
+    hipError_t r = hipGetLastError();
+    if (r != hipSuccess || eks <= kEcDirectKs) return r;
+    const EcSumArgs sa{ea.Tp, (float *)(base + w.ts), eks, M, L.rank, ea.rp1};
+    const int n = M * (L.rank + 1);
+    hipLaunchKernelGGL(prefill_ec_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, s, sa);
+    return hipGetLastError();
+  };
+  // the GEMM, then (split) the finish kernel over the partials; `epi` adds
+  // U B^T in the GEMM's own epilogue when it is not split
+  auto launch_main = [&](bool with_ec) {
+    const bool epi = with_ec && !split;
+    if (dtype == DT_F16)
+      L.per_channel ? launch_gemm<DT_F16, true>(g, ggrid, epi, main_s)
+                    : launch_gemm<DT_F16, false>(g, ggrid, epi, main_s);
+    else
+      L.per_channel ? launch_gemm<DT_BF16, true>(g, ggrid, epi, main_s)
+                    : launch_gemm<DT_BF16, false>(g, ggrid, epi, main_s);
+    hipError_t r = hipGetLastError();
+    if (r != hipSuccess || !split) return r;
+    if (dtype == DT_F16)
+      launch_finish<DT_F16, true>(fa, fgrid, L.per_channel, with_ec, main_s);
+    else
+      launch_finish<DT_BF16, true>(fa, fgrid, L.per_channel, with_ec, main_s);
     return hipGetLastError();
   };
 
   if (!concurrent) {
-    // serial: U first, then the GEMM adds U B^T in its epilogue
     if (ec && (e = launch_ec(main_s)) != hipSuccess) return e;
-    if (dtype == DT_F16)
-      launch_gemm_dt<DT_F16>(g, ggrid, L.per_channel, ec, main_s);
-    else
-      launch_gemm_dt<DT_BF16>(g, ggrid, L.per_channel, ec, main_s);
-    return hipGetLastError();
+    return launch_main(ec);
   }
 
-  // concurrent: EC on aux alongside the GEMM, merge after the join
+  // concurrent: compensator on aux alongside the GEMM; U B^T after the join
   std::lock_guard<std::mutex> lock(g_event_mu);
-  StreamEvents *ev = nullptr;
-  if ((e = get_events(&ev)) != hipSuccess) return e;
-  if ((e = hipEventRecord(ev->fork, main_s)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(aux_s, ev->fork, 0)) != hipSuccess) return e;
+  StreamEvents *evs = nullptr;
+  if ((e = get_events(&evs)) != hipSuccess) return e;
+  if ((e = hipEventRecord(evs->fork, main_s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(aux_s, evs->fork, 0)) != hipSuccess) return e;
   if ((e = launch_ec(aux_s)) != hipSuccess) return e;
-  if ((e = hipEventRecord(ev->join, aux_s)) != hipSuccess) return e;
+  if ((e = hipEventRecord(evs->join, aux_s)) != hipSuccess) return e;
+  if (split) {
+    // the finish kernel both sums the partials and adds U B^T: join first
+    if (dtype == DT_F16)
+      L.per_channel ? launch_gemm<DT_F16, true>(g, ggrid, false, main_s)
+                    : launch_gemm<DT_F16, false>(g, ggrid, false, main_s);
+    else
+      L.per_channel ? launch_gemm<DT_BF16, true>(g, ggrid, false, main_s)
+                    : launch_gemm<DT_BF16, false>(g, ggrid, false, main_s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(main_s, evs->join, 0)) != hipSuccess) return e;
+    if (dtype == DT_F16)
+      launch_finish<DT_F16, true>(fa, fgrid, L.per_channel, true, main_s);
+    else
+      launch_finish<DT_BF16, true>(fa, fgrid, L.per_channel, true, main_s);
+    return hipGetLastError();
+  }
+  if ((e = launch_main(false)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(main_s, evs->join, 0)) != hipSuccess) return e;
   if (dtype == DT_F16)
-    launch_gemm_dt<DT_F16>(g, ggrid, L.per_channel, false, main_s);
+    launch_finish<DT_F16, false>(fa, fgrid, false, true, main_s);
   else
-    launch_gemm_dt<DT_BF16>(g, ggrid, L.per_channel, false, main_s);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(main_s, ev->join, 0)) != hipSuccess) return e;
-  MergeArgs ma{y, L.B, U, L.N, M, L.rank, rp};
-  const dim3 mgrid((L.N + kMgT - 1) / kMgT, (M + kMgT - 1) / kMgT);
-  const size_t mlds = merge_lds_bytes(rp);
-  return dtype == DT_F16 ? launch_merge<DT_F16>(ma, mgrid, mlds, main_s)
-                         : launch_merge<DT_BF16>(ma, mgrid, mlds, main_s);
+    launch_finish<DT_BF16, false>(fa, fgrid, false, true, main_s);
+  return hipGetLastError();
 }
 
 }  // namespace spear

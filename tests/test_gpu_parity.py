@@ -234,6 +234,11 @@ PREFILL_CASES = [
     (128, 256, 128, 0, 100, "f16", False, True),   # rank 0
     (64, 128, 128, 4, 33, "f16", False, True),     # M just above the decode range
     (200, 512, 128, 100, 77, "f16", False, True),  # rank 100: padded U rows, 7 row blocks of [A; w_g]
+    (256, 4096, 128, 32, 100, "f16", True, False),  # 2 output tiles: K split 8 ways, serial
+    (136, 4096, 0, 16, 40, "bf16", True, False),    # K split, per-channel, ragged N
+    (256, 4096, 128, 32, 100, "f16", True, True),   # K split untouched by the concurrent schedule
+    (192, 8192, 0, 64, 40, "f16", True, False),     # few tokens: compensator split 32 ways, summed once
+    (192, 8192, 0, 64, 40, "f16", True, True),      # the same, concurrent schedule
 ]
 
 
@@ -277,6 +282,40 @@ def test_decode_and_prefill_agree_and_dispatch():
     assert_close(gpu_y_f64(yp, "f16"), ref[:32], "prefill")
     assert torch.equal(yl32.view(torch.int16), yd.view(torch.int16))     # M = 32 -> decode
     assert torch.equal(yl48.view(torch.int16), yp48.view(torch.int16))   # M = 48 -> prefill
+
+
+def test_prefill_rank0_split_k_with_and_without_workspace():
+    """Rank 0: with a workspace the GEMM splits K (2 output tiles, 8 splits), without one
+    it does not; both match the oracle and each other within the tolerance."""
+    note("prefill rank 0, split K")
+    hl, xb, lay, x = _setup(256, 4096, 128, 0, seed=31, M=70, outliers=True)
+    ref = oracle_y(hl, xb)
+    ws = spear.new_workspace(lay, 70)
+    y_split = spear.spear_linear_prefill(lay, x, workspace=ws)
+    y_plain = spear.spear_linear_prefill(lay, x)
+    torch.cuda.synchronize()
+    assert_close(gpu_y_f64(y_split, "f16"), ref, "split")
+    assert_close(gpu_y_f64(y_plain, "f16"), ref, "unsplit")
+
+
+def test_workspace_shared_by_layers():
+    """One workspace, sized for the larger of two layers, serves both in any order."""
+    note("workspace shared by two layers")
+    h1, x1b, l1, x1 = _setup(264, 4096, 128, 32, seed=41, M=96, outliers=True)
+    h2, x2b, l2, x2 = _setup(1000, 1024, 0, 16, seed=42, M=96, outliers=False)
+    n = max(spear.spear_workspace_bytes(l1, 96), spear.spear_workspace_bytes(l2, 96))
+    buf = torch.zeros(n + 256, dtype=torch.uint8, device="cuda")
+    off = (-buf.data_ptr()) % 256
+    ws = buf[off:off + n]
+    r1, r2 = oracle_y(h1, x1b), oracle_y(h2, x2b)
+    outs = []
+    for it, (which, M) in enumerate([(1, 96), (2, 96), (1, 8), (2, 40), (1, 50), (2, 3), (1, 96)]):
+        lay, x = (l1, x1) if which == 1 else (l2, x2)
+        outs.append((which, M, spear.spear_linear(lay, x[:M].contiguous(), workspace=ws)))
+    torch.cuda.synchronize()
+    for which, M, y in outs:
+        assert_close(gpu_y_f64(y, "f16"), (r1 if which == 1 else r2)[:M], f"layer {which} M={M}")
+    assert spear.spear_workspace_flags(ws) == 0
 
 
 def test_workspace_shared_by_prefill_and_decode():
