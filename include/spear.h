@@ -85,7 +85,30 @@ typedef void *spear_stream_t; /* a hipStream_t */
  *   w_gate      [K] activation type (gate weights).
  *   b_gate      gate bias; +INFINITY gives g == 1 and -INFINITY gives g == 0
  *               exactly (for finite w_gate . x).
+ *   rank_gate   optional per-rank gate (see spear_rank_gate_t); r > 0 only.
  */
+/*
+ * The pages' per-rank gate (2.1 A: the compensator applies an input-adaptive
+ * gate gamma(A x) to each of the r rank components, with a strength alpha).
+ * gamma is read as a bottleneck MLP r -> hidden -> r:
+ *
+ *     t = A x,  gamma(t) = sigmoid(W2 relu(W1 t + b1) + b2),
+ *     y = dequant(W_q) x + alpha * B (gamma(t) * t)      (elementwise product)
+ *
+ * All arrays are fp32 device memory: W1 [hidden][r], b1 [hidden],
+ * W2 [r][hidden], b2 [r], row-major.  1 <= hidden <= SPEAR_MAX_GATE_HIDDEN.
+ * The struct itself is host memory, read during the call only.
+ */
+#define SPEAR_MAX_GATE_HIDDEN 64
+typedef struct spear_rank_gate {
+  int32_t hidden;
+  const float *W1;
+  const float *b1;
+  const float *W2;
+  const float *b2;
+  float alpha;
+} spear_rank_gate_t;
+
 typedef struct spear_layer {
   int32_t N, K, group_size;
   const int32_t *qweight;
@@ -96,6 +119,9 @@ typedef struct spear_layer {
   const void *B;
   const void *w_gate;
   float b_gate;
+  /* NULL: the scalar gate sigmoid(w_gate . x + b_gate).  Otherwise the
+   * per-rank gate above, and w_gate / b_gate are ignored (may be NULL). */
+  const spear_rank_gate_t *rank_gate;
 } spear_layer_t;
 
 #define SPEAR_MAX_RANK 128

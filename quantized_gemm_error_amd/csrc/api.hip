@@ -54,13 +54,26 @@ spear_status_t check_layer(const spear_layer_t *layer, LayerDesc *d) {
   if (l.rank < 0 || l.rank > SPEAR_MAX_RANK)
     return fail(l.rank < 0 ? SPEAR_ERR_INVALID_ARGUMENT : SPEAR_ERR_UNSUPPORTED,
                 "rank=%d outside 0..%d", l.rank, SPEAR_MAX_RANK);
+  const spear_rank_gate_t *rg = l.rank > 0 ? l.rank_gate : nullptr;
   if (l.rank > 0) {
-    if (!l.A || !l.B || !l.w_gate)
-      return fail(SPEAR_ERR_INVALID_ARGUMENT, "rank>0 needs A, B and w_gate");
-    if (!aligned(l.A, 16) || !aligned(l.w_gate, 16))
-      return fail(SPEAR_ERR_INVALID_ARGUMENT, "A and w_gate must be 16-byte aligned");
+    if (!l.A || !l.B) return fail(SPEAR_ERR_INVALID_ARGUMENT, "rank>0 needs A and B");
+    if (!aligned(l.A, 16)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "A must be 16-byte aligned");
     if (!aligned(l.B, 2)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "B not 2-byte aligned");
-    if (isnan(l.b_gate)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "b_gate is NaN");
+    if (!rg) {
+      if (!l.w_gate) return fail(SPEAR_ERR_INVALID_ARGUMENT, "the scalar gate needs w_gate");
+      if (!aligned(l.w_gate, 16))
+        return fail(SPEAR_ERR_INVALID_ARGUMENT, "w_gate must be 16-byte aligned");
+      if (isnan(l.b_gate)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "b_gate is NaN");
+    } else {
+      if (rg->hidden < 1 || rg->hidden > SPEAR_MAX_GATE_HIDDEN)
+        return fail(rg->hidden < 1 ? SPEAR_ERR_INVALID_ARGUMENT : SPEAR_ERR_UNSUPPORTED,
+                    "rank_gate hidden=%d outside 1..%d", rg->hidden, SPEAR_MAX_GATE_HIDDEN);
+      if (!rg->W1 || !rg->b1 || !rg->W2 || !rg->b2)
+        return fail(SPEAR_ERR_INVALID_ARGUMENT, "rank_gate needs W1, b1, W2 and b2");
+      if (!aligned(rg->W1, 4) || !aligned(rg->b1, 4) || !aligned(rg->W2, 4) || !aligned(rg->b2, 4))
+        return fail(SPEAR_ERR_INVALID_ARGUMENT, "rank_gate arrays not 4-byte aligned");
+      if (!isfinite(rg->alpha)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "rank_gate alpha not finite");
+    }
   }
   d->N = l.N;
   d->K = l.K;
@@ -75,6 +88,16 @@ spear_status_t check_layer(const spear_layer_t *layer, LayerDesc *d) {
   d->B = (const uint16_t *)l.B;
   d->wg = (const uint16_t *)l.w_gate;
   d->b_gate = l.b_gate;
+  d->rg_hidden = rg ? rg->hidden : 0;
+  d->rg_W1 = rg ? rg->W1 : nullptr;
+  d->rg_b1 = rg ? rg->b1 : nullptr;
+  d->rg_W2 = rg ? rg->W2 : nullptr;
+  d->rg_b2 = rg ? rg->b2 : nullptr;
+  d->rg_alpha = rg ? rg->alpha : 1.f;
+  if (rg) {
+    d->wg = nullptr;
+    d->b_gate = 0.f;
+  }
   return SPEAR_OK;
 }
 

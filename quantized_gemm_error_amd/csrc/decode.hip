@@ -69,6 +69,12 @@ struct DecodeArgs {
   int sz_off;      // byte offset of the scale/zero table in dynamic LDS
   int gmul;        // ceil(2^20 / (G / 128)): kb * gmul >> 20 == kb / (G / 128)
   int ks;          // producer K-splits per 16-row block of [A; w_g] (a multiple of 4)
+  int rows;        // rows of [A; w_g]: rank + 1, or rank with the per-rank gate
+  // per-rank gate (rg_hidden > 0): u = alpha gamma(t) * t, t = A x
+  int rg_hidden;
+  const float *rg_W1, *rg_b1, *rg_W2, *rg_b2;
+  float rg_alpha;
+  int rg_off;      // byte offset of its scratch in dynamic LDS
   int part_bytes;  // bytes of the partial-sum array
   int red_off;     // byte offset of the wave-reduction buffer in dynamic LDS
   WsHeader *hdr;
@@ -99,8 +105,9 @@ __device__ void produce(const DecodeArgs &a, int p, f32x4_t (*red)[MB][64], int 
   const int col = lane & 15, h = lane >> 4;
   const int rb = p / a.ks, ksi = p % a.ks;
   const int j = rb * 16 + col;  // row of [A; w_g]
-  const bool jin = j <= a.rank;
-  const uint16_t *arow = (j < a.rank) ? a.A + (size_t)j * a.K : a.wg;
+  const bool jin = j < a.rows;
+  // j >= rank: w_g, or (per-rank gate, no w_g) any valid row, masked by jin
+  const uint16_t *arow = (j < a.rank) ? a.A + (size_t)j * a.K : (a.wg ? a.wg : a.A);
   const int nsteps = a.K / 32;
   const int per = (nsteps + a.ks - 1) / a.ks;
   const int s0 = ksi * per;
@@ -309,6 +316,57 @@ __device__ __forceinline__ void chunk_store(const DecodeArgs &a, const XChunk &c
 }
 
 // ---------------------------------------------------------------------------
+// The pages' per-rank gate in a consumer's epilogue, after the producers are
+// in: the workgroup gathers t = A x for every token (the sum of each
+// element's K-split partials, in split order), computes
+// hidden = relu(W1 t + b1), gamma = sigmoid(W2 hidden + b2) and
+// u = alpha gamma * t in LDS, and each wave adds u B^T for its rank steps.
+// ---------------------------------------------------------------------------
+template <int DT, int MB, int KG>
+__device__ void rank_gate_epilogue(const DecodeArgs &a, uint16_t *xs, f32x4_t (&acc)[MB], int row,
+                                   int wk, int tid) {
+  const int lane = tid & 63, col = lane & 15, h = lane >> 4;
+  const int PS = 16 * MB;
+  const int rs = a.rank + 1, hs = a.rg_hidden + 1;
+  float *tl = (float *)((char *)xs + a.rg_off);  // [16 MB][rs]
+  float *hl = tl + PS * rs;                       // [16 MB][hs]
+  for (int i = tid; i < a.M * a.rank; i += kThreads) {
+    const int m = i / a.rank, j = i - m * a.rank;
+    const uint32_t *pp = (const uint32_t *)a.part + (size_t)(j * PS + m) * a.ks;
+    float t = 0.f;
+    for (int q = 0; q < a.ks; ++q)
+      t += bitcast<float>(__hip_atomic_load(pp + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    tl[m * rs + j] = t;
+  }
+  __syncthreads();
+  for (int i = tid; i < a.M * a.rg_hidden; i += kThreads) {
+    const int m = i / a.rg_hidden, c = i - m * a.rg_hidden;
+    float v = a.rg_b1[c];
+    for (int k = 0; k < a.rank; ++k) v += a.rg_W1[(size_t)c * a.rank + k] * tl[m * rs + k];
+    hl[m * hs + c] = v > 0.f ? v : 0.f;
+  }
+  __syncthreads();
+  for (int i = tid; i < a.M * a.rank; i += kThreads) {
+    const int m = i / a.rank, j = i - m * a.rank;
+    float v = a.rg_b2[j];
+    for (int c = 0; c < a.rg_hidden; ++c) v += a.rg_W2[(size_t)j * a.rg_hidden + c] * hl[m * hs + c];
+    tl[m * rs + j] *= a.rg_alpha * gate_sigmoid(v);
+  }
+  __syncthreads();
+  const int nst = (a.rank + 3) / 4;
+  for (int st = wk; st < nst; st += KG) {
+    const int j = 4 * st + h;
+    const bool jin = j < a.rank;
+    const float bval = jin ? to_f32<DT>(a.B[(size_t)row * a.rank + j]) : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = col + 16 * mb;
+      acc[mb] = mfma_16x16x4_f32((jin && m < a.M) ? tl[m * rs + j] : 0.f, bval, acc[mb]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Consumers: 16 * WR output rows, full K.  The eight waves form WR row-blocks
 // of KG = 8 / WR waves; the KG waves of a row-block take interleaved K blocks
 // and all waves share the staged activation.
@@ -468,6 +526,9 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
     float b_first = 0.f;
     if (wk < nst) b_first = to_f32<DT>(a.B[(size_t)row * a.rank + min(4 * wk + h, a.rank - 1)]);
     wait_producers(a, tid);
+    if (a.rg_hidden > 0) {
+      rank_gate_epilogue<DT, MB, KG>(a, xs, acc, row, wk, tid);
+    } else {
     const __amdgpu_buffer_rsrc_t pr =
         __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
     const int kq = a.ks / 4;
@@ -521,6 +582,7 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
         step(st, to_f32<DT>(a.B[(size_t)row * a.rank + min(4 * st + h, a.rank - 1)]),
              std::false_type{});
     }
+    }  // scalar gate
   }
 
   // fixed-order sum over the row-block's KG waves
@@ -657,7 +719,7 @@ static int resident_per_cu(const DecodePlan &p) {
 static DecodePlan plan_for(const LayerDesc &L, int M, int wr) {
   DecodePlan p{};
   p.mb = M <= 16 ? 1 : 2;
-  p.rb_a = L.rank > 0 ? (L.rank + 1 + 15) / 16 : 0;
+  p.rb_a = L.rank > 0 ? (L.rank + L.gate_rows() + 15) / 16 : 0;
   p.ks = L.rank > 0 ? decode_ksplit(L.K) : 0;
   p.producers = p.rb_a * p.ks;
   p.nb = (L.K + 127) / 128;
@@ -697,6 +759,10 @@ static DecodePlan plan_for(const LayerDesc &L, int M, int wr) {
   if (!L.per_channel) p.lds = p.sz_off + (size_t)16 * wr * L.ngroups * 8;
   p.red_off = (int)((p.lds + 15) / 16 * 16);
   p.lds = p.red_off + (size_t)kWaves * p.mb * 64 * 16;
+  if (L.rank > 0 && L.rg_hidden > 0) {  // per-rank gate scratch: t and hidden for 16 mb tokens
+    p.rg_off = (int)((p.lds + 15) / 16 * 16);
+    p.lds = p.rg_off + (size_t)16 * p.mb * (L.rank + 1 + L.rg_hidden + 1) * sizeof(float);
+  }
   p.n_tiles = (L.N + 16 * wr - 1) / (16 * wr);
   p.ok = p.lds <= (size_t)kMaxLds;
   return p;
@@ -760,6 +826,14 @@ hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint1
   a.gmul = L.per_channel ? 0 : (int)(((1u << 20) + (uint32_t)(L.G / 128) - 1) / (uint32_t)(L.G / 128));
   a.red_off = p.red_off;
   a.ks = p.ks;
+  a.rows = L.rank + L.gate_rows();
+  a.rg_hidden = L.rg_hidden;
+  a.rg_W1 = L.rg_W1;
+  a.rg_b1 = L.rg_b1;
+  a.rg_W2 = L.rg_W2;
+  a.rg_b2 = L.rg_b2;
+  a.rg_alpha = L.rg_alpha;
+  a.rg_off = p.rg_off;
   a.part_bytes = (int)((size_t)p.producers * 16 * (16 * p.mb) * sizeof(float));
   a.hdr = (WsHeader *)ws;
   a.part = ws ? (float *)((char *)ws + kWsDataOff) : nullptr;

@@ -42,6 +42,11 @@ struct LayerDesc {
   const uint16_t *scales, *zeros;
   const uint16_t *A, *B, *wg;
   float b_gate;
+  // per-rank gate (rg_hidden > 0): y += rg_alpha B (gamma(t) * t), t = A x
+  int rg_hidden;
+  const float *rg_W1, *rg_b1, *rg_W2, *rg_b2;
+  float rg_alpha;
+  int gate_rows() const { return rg_hidden > 0 ? 0 : 1; }  // rows of [A; w_g] past A
 };
 
 // Derived decode launch geometry.
@@ -61,6 +66,7 @@ struct DecodePlan {
   int nbw_pad;     // block iterations rounded up to a multiple of the ring depth
   int sz_off;      // byte offset of the scale/zero table in dynamic LDS
   int red_off;     // byte offset of the wave-reduction buffer in dynamic LDS
+  int rg_off;      // per-rank gate scratch (0 when the layer has none)
   size_t lds;      // dynamic LDS bytes
 };
 

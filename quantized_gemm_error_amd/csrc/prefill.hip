@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 struct EcArgs {
   const uint16_t *x, *A, *wg;
-  int K, M, rank, rp1, ks;
+  int K, M, rank, rows, rp1, ks;  // rows of [A; w_g]: rank + 1, or rank (per-rank gate)
   float *Tp;  // [ks][M][rp1]
 };
 
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64 * kEcWaves) void prefill_ec_kernel(EcArgs a) {
   const uint16_t *xrow[kEcMb];
 #pragma unroll
   for (int mb = 0; mb < kEcMb; ++mb) xrow[mb] = a.x + (size_t)min(m0 + col + 16 * mb, a.M - 1) * a.K;
-  const int rb_a = (a.rank + 16) / 16;
+  const int rb_a = (a.rows + 15) / 16;
   const int nsteps = a.K / 32;
   const int per = (nsteps + a.ks - 1) / a.ks;
   const int s_lo = ksi * per, s_hi = min(nsteps, s_lo + per);
@@ -334,8 +334,9 @@ __global__ __launch_bounds__(64 * kEcWaves) void prefill_ec_kernel(EcArgs a) {
 #pragma unroll
     for (int r = 0; r < kEcRb; ++r) {
       const int j = (rb0 + r) * 16 + col;
-      jin[r] = rb0 + r < rb_a && j <= a.rank;
-      arow[r] = (j < a.rank) ? a.A + (size_t)j * a.K : a.wg;  // j >= rank: w_g (masked if past it)
+      jin[r] = rb0 + r < rb_a && j < a.rows;
+      // j >= rank: w_g, or (per-rank gate, no w_g) any valid row; masked past the rows
+      arow[r] = (j < a.rank) ? a.A + (size_t)j * a.K : (a.wg ? a.wg : a.A);
     }
     f32x4_t acc[kEcRb][kEcMb];
 #pragma unroll
@@ -392,13 +393,58 @@ __global__ __launch_bounds__(64 * kEcWaves) void prefill_ec_kernel(EcArgs a) {
   }
 
 
-  // this split's sums, rows 0..rank of its tokens
-  const int nval = kEcTok * (a.rank + 1);
+  // this split's sums, rows 0..rows-1 of its tokens
+  const int nval = kEcTok * a.rows;
   float *tp = a.Tp + ((size_t)ksi * a.M + m0) * a.rp1;
   for (int i = tid; i < nval; i += 64 * kEcWaves) {
-    const int mm = i / (a.rank + 1), j = i - mm * (a.rank + 1);
+    const int mm = i / a.rows, j = i - mm * a.rows;
     if (m0 + mm < a.M) tp[(size_t)mm * a.rp1 + j] = tz[mm][j];
   }
+}
+
+// The pages' per-rank gate: for each token, t = the sum of its split
+// partials (rows 0..rank-1, split order), hidden = relu(W1 t + b1),
+// gamma = sigmoid(W2 hidden + b2), and Ts[m][j] = alpha gamma_j t_j.  Column
+// rank of Ts is set to +infinity, so that consumers, which apply the scalar
+// gate sigmoid(Ts[m][rank] + 0), multiply by exactly 1.
+struct RgArgs {
+  const float *Tp;
+  float *Ts;  // [M][rp1]
+  int ks, M, rank, rp1, hidden;
+  const float *W1, *b1, *W2, *b2;
+  float alpha;
+};
+constexpr int kRgTok = 8;  // tokens per workgroup
+
+__global__ __launch_bounds__(256) void prefill_rgate_kernel(RgArgs a) {
+  __shared__ float tl[kRgTok][SPEAR_MAX_RANK + 1];
+  __shared__ float hl[kRgTok][SPEAR_MAX_GATE_HIDDEN + 1];
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.x * kRgTok;
+  for (int i = tid; i < kRgTok * a.rank; i += 256) {
+    const int mm = i / a.rank, j = i - mm * a.rank;
+    float t = 0.f;
+    if (m0 + mm < a.M)
+      for (int q = 0; q < a.ks; ++q) t += a.Tp[((size_t)q * a.M + m0 + mm) * a.rp1 + j];
+    tl[mm][j] = t;
+  }
+  __syncthreads();
+  for (int i = tid; i < kRgTok * a.hidden; i += 256) {
+    const int mm = i / a.hidden, c = i - mm * a.hidden;
+    float v = a.b1[c];
+    for (int k = 0; k < a.rank; ++k) v += a.W1[(size_t)c * a.rank + k] * tl[mm][k];
+    hl[mm][c] = v > 0.f ? v : 0.f;
+  }
+  __syncthreads();
+  for (int i = tid; i < kRgTok * a.rank; i += 256) {
+    const int mm = i / a.rank, j = i - mm * a.rank;
+    const int m = m0 + mm;
+    if (m >= a.M) continue;
+    float v = a.b2[j];
+    for (int c = 0; c < a.hidden; ++c) v += a.W2[(size_t)j * a.hidden + c] * hl[mm][c];
+    a.Ts[(size_t)m * a.rp1 + j] = a.alpha * gate_sigmoid(v) * tl[mm][j];
+  }
+  if (tid < kRgTok && m0 + tid < a.M) a.Ts[(size_t)(m0 + tid) * a.rp1 + a.rank] = __builtin_inff();
 }
 
 // Sum of the compensator's split partials, Ts[m][j] = sum_q Tp[q][m][j] in
@@ -668,14 +714,16 @@ hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint
   EcView ev{};
   EcArgs ea{};
   int eks = 1;
+  const bool rgate = ec && L.rg_hidden > 0;
   if (ec) {
     const int rp1 = rank_pad(L.rank + 1);
     eks = ec_ksplit(M, L.K);
-    ea = EcArgs{x, L.A, L.wg, L.K, M, L.rank, rp1, eks, (float *)(base + w.tp)};
-    // consumers read the split partials directly, or their one-time sum
-    ev = eks <= kEcDirectKs
+    ea = EcArgs{x, L.A, L.wg, L.K, M, L.rank, L.rank + L.gate_rows(), rp1, eks, (float *)(base + w.tp)};
+    // consumers read the split partials directly, or their one-time sum (or,
+    // with the per-rank gate, the gated U with a gate column of +infinity)
+    ev = (eks <= kEcDirectKs && !rgate)
              ? EcView{(const float *)(base + w.tp), eks, M, L.rank, rp1, L.b_gate}
-             : EcView{(const float *)(base + w.ts), 1, M, L.rank, rp1, L.b_gate};
+             : EcView{(const float *)(base + w.ts), 1, M, L.rank, rp1, rgate ? 0.f : L.b_gate};
   }
   // split K only with a workspace (a rank-0 call may come without one)
   const int gks = ws ? gemm_ksplit(M, L.N, L.K) : 1;
@@ -694,7 +742,14 @@ hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint
     else
       hipLaunchKernelGGL(prefill_ec_kernel<DT_BF16>, egrid, dim3(64 * kEcWaves), 0, s, ea);
     hipError_t r = hipGetLastError();
-    if (r != hipSuccess || eks <= kEcDirectKs) return r;
+    if (r != hipSuccess) return r;
+    if (rgate) {
+      const RgArgs ra{ea.Tp, (float *)(base + w.ts), eks, M, L.rank, ea.rp1, L.rg_hidden,
+                      L.rg_W1, L.rg_b1, L.rg_W2, L.rg_b2, L.rg_alpha};
+      hipLaunchKernelGGL(prefill_rgate_kernel, dim3((M + kRgTok - 1) / kRgTok), dim3(256), 0, s, ra);
+      return hipGetLastError();
+    }
+    if (eks <= kEcDirectKs) return r;
     const EcSumArgs sa{ea.Tp, (float *)(base + w.ts), eks, M, L.rank, ea.rp1};
     const int n = M * (L.rank + 1);
     hipLaunchKernelGGL(prefill_ec_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, s, sa);

@@ -39,6 +39,14 @@ class SpearError(RuntimeError):
         self.status = status
 
 
+class SpearRankGateC(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+        ("b2", ctypes.c_void_p), ("alpha", ctypes.c_float),
+    ]
+
+
 class SpearLayerC(ctypes.Structure):
     _fields_ = [
         ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("group_size", ctypes.c_int32),
@@ -46,6 +54,7 @@ class SpearLayerC(ctypes.Structure):
         ("rank", ctypes.c_int32),
         ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
         ("b_gate", ctypes.c_float),
+        ("rank_gate", ctypes.POINTER(SpearRankGateC)),
     ]
 
 
@@ -120,6 +129,19 @@ def _dtype_code(t) -> int:
 
 
 @dataclass
+class RankGate:
+    """The per-rank gate gamma(t) = sigmoid(W2 relu(W1 t + b1) + b2) (see spear_rank_gate_t);
+    W1 [hidden][r], b1 [hidden], W2 [r][hidden], b2 [r]: float32 device tensors."""
+
+    hidden: int
+    W1: object
+    b1: object
+    W2: object
+    b2: object
+    alpha: float = 1.0
+
+
+@dataclass
 class SpearLayer:
     """Device tensors of one compensated 4-bit layer (see spear_layer_t)."""
 
@@ -134,11 +156,18 @@ class SpearLayer:
     B: object = None            # [N][r]
     w_gate: object = None       # [K]
     b_gate: float = 0.0
+    rank_gate: object = None    # RankGate, or None for the scalar gate
 
     def as_c(self) -> SpearLayerC:
-        return SpearLayerC(self.N, self.K, self.group_size, _ptr(self.qweight), _ptr(self.scales),
-                           _ptr(self.zeros), self.rank, _ptr(self.A), _ptr(self.B),
-                           _ptr(self.w_gate), float(self.b_gate))
+        c = SpearLayerC(self.N, self.K, self.group_size, _ptr(self.qweight), _ptr(self.scales),
+                        _ptr(self.zeros), self.rank, _ptr(self.A), _ptr(self.B),
+                        _ptr(self.w_gate), float(self.b_gate), None)
+        if self.rank_gate is not None:
+            g = self.rank_gate
+            c._rg = SpearRankGateC(int(g.hidden), _ptr(g.W1), _ptr(g.b1), _ptr(g.W2), _ptr(g.b2),
+                                   float(g.alpha))  # kept alive with the struct
+            c.rank_gate = ctypes.pointer(c._rg)
+        return c
 
     def without_compensator(self) -> "SpearLayer":
         return SpearLayer(self.N, self.K, self.group_size, self.qweight, self.scales, self.zeros)
@@ -270,6 +299,17 @@ def layer_to_device(host_layer, device="cuda", stream=None) -> SpearLayer:
         lay.B = up(host_layer.B, act)
         lay.w_gate = up(host_layer.w_gate, act)
     return lay
+
+
+def rank_gate_to_device(params, alpha: float = 1.0, device="cuda") -> RankGate:
+    """float32 numpy W1, b1, W2, b2 (as from synth.make_rank_gate) -> a RankGate on the device."""
+    import numpy as np
+    import torch
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    return RankGate(hidden=int(params["W1"].shape[0]), W1=up(params["W1"]), b1=up(params["b1"]),
+                    W2=up(params["W2"]), b2=up(params["b2"]), alpha=float(alpha))
 
 
 def act_to_device(bits, dtype: str, device="cuda"):

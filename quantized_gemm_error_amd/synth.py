@@ -131,6 +131,18 @@ def make_layer(N: int, K: int, group_size: int, rank: int, seed: int, dtype: str
                       w_fp32=w if keep_fp32 else None)
 
 
+def make_rank_gate(rank: int, hidden: int, seed: int, t_scale: float = 1.0):
+    """The per-rank gate's MLP parameters, float32: W1 [hidden][rank] ~ N(0, 1/(rank t_scale^2)),
+    b1 ~ N(0, 0.1), W2 [rank][hidden] ~ N(0, 1/hidden), b2 ~ N(0, 0.5).  t_scale is the
+    typical size of a component of t = A x, so that the gate is not saturated."""
+    rng = np.random.default_rng(seed + 31337)
+    W1 = (rng.standard_normal((hidden, rank), dtype=np.float32) / np.float32(np.sqrt(rank) * t_scale))
+    b1 = rng.standard_normal(hidden, dtype=np.float32) * np.float32(0.1)
+    W2 = rng.standard_normal((rank, hidden), dtype=np.float32) / np.float32(np.sqrt(hidden))
+    b2 = rng.standard_normal(rank, dtype=np.float32) * np.float32(0.5)
+    return dict(W1=W1, b1=b1, W2=W2, b2=b2)
+
+
 def outlier_channels(K: int, seed: int, frac: float = 0.01) -> np.ndarray:
     """round(frac*K) distinct input-channel indices, fixed by the seed."""
     n_out = int(round(frac * K))

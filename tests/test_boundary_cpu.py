@@ -105,6 +105,36 @@ def test_decode_rejects_bad_layer(lib, bad, code):
     assert lib.spear_last_error().decode() != ""
 
 
+def _rank_gate(**kw):
+    g = spear.SpearRankGateC(hidden=16, W1=FAKE, b1=FAKE, W2=FAKE, b2=FAKE, alpha=1.0)
+    for k, v in kw.items():
+        setattr(g, k, v)
+    return g
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(hidden=0), 1), (dict(hidden=65), 2), (dict(W1=None), 1), (dict(b2=None), 1),
+    (dict(W2=FAKE + 2), 1), (dict(alpha=math.nan), 1), (dict(alpha=math.inf), 1),
+])
+def test_decode_rejects_bad_rank_gate(lib, bad, code):
+    g = _rank_gate(**bad)
+    lay = _layer(w_gate=None, b_gate=math.nan)   # ignored with a per-rank gate
+    lay.rank_gate = ctypes.pointer(g)
+    assert _decode(lib, lay) == code
+    assert lib.spear_last_error().decode() != ""
+
+
+def test_rank_gate_replaces_the_scalar_gate(lib):
+    # with a per-rank gate, w_gate and b_gate are not needed; validation passes (M = 0: no-op)
+    g = _rank_gate()
+    lay = _layer(w_gate=None, b_gate=math.nan)
+    lay.rank_gate = ctypes.pointer(g)
+    assert _decode(lib, lay, M=0) == 0
+    assert lib.spear_workspace_bytes(ctypes.byref(lay), 32) > 0
+    # without one, a missing w_gate is an error
+    assert _decode(lib, _layer(w_gate=None)) == 1
+
+
 def test_rejects_bad_io_and_workspace(lib):
     lay = _layer()
     assert _decode(lib, None) == 1

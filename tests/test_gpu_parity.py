@@ -164,6 +164,84 @@ def test_compensator_isolated(path):
     assert g.min() < 0.45 and g.max() > 0.55
 
 
+# ---------------------------------------------------------------------------
+# the pages' per-rank gate
+# ---------------------------------------------------------------------------
+
+RANK_GATE_CASES = [
+    # path, N, K, G, r, hidden, M, dtype, alpha
+    ("decode", 200, 1024, 128, 32, 16, 1, "f16", 0.7),
+    ("decode", 136, 2048, 0, 24, 8, 5, "bf16", 1.3),
+    ("decode", 96, 512, 128, 40, 64, 32, "f16", 1.0),
+    ("prefill", 264, 1024, 128, 32, 16, 70, "f16", 0.7),
+    ("prefill", 128, 4096, 128, 16, 32, 40, "bf16", 0.5),   # K split, many compensator splits
+    ("prefill_aux", 200, 1024, 0, 32, 16, 150, "f16", 1.0),
+]
+
+
+def _rank_gate_ref(hl, xb, params, alpha, rows=None):
+    sel = slice(None) if rows is None else np.asarray(rows)
+    return oracle.rank_gate_linear_ref(xb, oracle.pack_int4(hl.q[sel]), hl.scales[sel], hl.zeros[sel],
+                                       hl.group_size, hl.dtype, hl.A, hl.B[sel],
+                                       params["W1"].astype(np.float64), params["b1"].astype(np.float64),
+                                       params["W2"].astype(np.float64), params["b2"].astype(np.float64),
+                                       alpha)
+
+
+@pytest.mark.parametrize("path,N,K,G,r,hidden,M,dtype,alpha", RANK_GATE_CASES)
+def test_rank_gate_parity(path, N, K, G, r, hidden, M, dtype, alpha):
+    note(f"rank gate {path} N={N} K={K} r={r} h={hidden} M={M} {dtype}")
+    hl, xb, lay, x = _setup(N, K, G, r, seed=N + K + hidden, dtype=dtype, M=M, outliers=True)
+    params = synth.make_rank_gate(r, hidden, seed=N + r, t_scale=0.01 * np.sqrt(K))
+    lay.rank_gate = spear.rank_gate_to_device(params, alpha, DEV)
+    lay.w_gate, lay.b_gate = None, float("nan")          # ignored with a per-rank gate
+    ws = spear.new_workspace(lay, M)
+    if path == "decode":
+        y = spear.spear_linear_decode(lay, x, workspace=ws)
+    elif path == "prefill":
+        y = spear.spear_linear_prefill(lay, x, workspace=ws)
+    else:
+        y = spear.spear_linear_prefill(lay, x, workspace=ws, aux_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert_close(gpu_y_f64(y, dtype), _rank_gate_ref(hl, xb, params, alpha), f"rank gate {path}")
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_rank_gate_isolated(path):
+    """q == z: y is alpha B (gamma(t) t) alone, large, with gamma neither 0 nor 1 throughout."""
+    note(f"rank gate isolation {path}")
+    N, K, r, h, M = 144, 512, 32, 16, 7 if path == "decode" else 90
+    rng = np.random.default_rng(8)
+    zc = rng.integers(0, 16, size=(N, K // 128))
+    sK = 1.0 / np.sqrt(K)
+    hl = synth.SynthLayer(
+        N=N, K=K, group_size=128, rank=r, dtype="f16", q=np.repeat(zc, 128, axis=1).astype(np.uint8),
+        scales=synth.to_f16_bits(rng.uniform(0.005, 0.02, (N, K // 128)).astype(np.float32)),
+        zeros=synth.to_f16_bits(zc.astype(np.float32)),
+        A=synth.to_f16_bits(rng.standard_normal((r, K)).astype(np.float32) * sK),
+        B=synth.to_f16_bits(rng.standard_normal((N, r)).astype(np.float32)),
+        w_gate=None, b_gate=0.0)
+    params = synth.make_rank_gate(r, h, seed=9, t_scale=1.0)
+    xb = synth.make_activations(M, K, seed=10)
+    q = torch.from_numpy(hl.q).to(DEV)
+    lay = spear.SpearLayer(N=N, K=K, group_size=128, qweight=spear.spear_pack_int4(q),
+                           scales=spear.act_to_device(hl.scales, "f16", DEV),
+                           zeros=spear.act_to_device(hl.zeros, "f16", DEV), rank=r,
+                           A=spear.act_to_device(hl.A, "f16", DEV), B=spear.act_to_device(hl.B, "f16", DEV),
+                           rank_gate=spear.rank_gate_to_device(params, 0.8, DEV))
+    x = spear.act_to_device(xb, "f16", DEV)
+    ws = spear.new_workspace(lay, M)
+    y = run(path, lay, x, ws)
+    torch.cuda.synchronize()
+    ref = _rank_gate_ref(hl, xb, params, 0.8)
+    assert np.max(np.abs(ref)) > 1.0
+    assert_close(gpu_y_f64(y, "f16"), ref, f"rank gate isolation {path}")
+    t = oracle.f16_bits_to_f64(xb) @ oracle.f16_bits_to_f64(hl.A).T
+    gam = oracle.sigmoid(np.maximum(t @ params["W1"].T.astype(np.float64) + params["b1"], 0)
+                         @ params["W2"].T.astype(np.float64) + params["b2"])
+    assert gam.min() < 0.3 and gam.max() > 0.7
+
+
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 def test_full_rank_absorption(path):
     """g = 1, A = I, B = fp16(W - dequant(W_q)): recovers the fp16 product."""
@@ -217,6 +295,25 @@ def test_decode_workspace_reuse_many_calls():
     torch.cuda.synchronize()
     for (it, M), y in outs.items():
         assert_close(gpu_y_f64(y, "f16"), ref[:M], f"call {it} M={M}")
+    assert spear.spear_workspace_flags(ws) == 0
+    assert _ws_header(ws) == [0] * 11
+
+
+def test_decode_fresh_inputs_every_call():
+    """Consecutive calls on one workspace with different activations each time: a
+    partial sum left by an earlier call would show up as a wrong output."""
+    note("decode, fresh inputs every call")
+    hl, _, lay, _ = _setup(288, 2048, 128, 32, seed=51, M=1, outliers=True)
+    ws = spear.new_workspace(lay, 32)
+    cases = []
+    for it in range(24):
+        M = [1, 3, 16, 32][it % 4]
+        xb = synth.make_activations(M, 2048, seed=1000 + it, dtype="f16", outliers=True)
+        x = spear.act_to_device(xb, "f16", DEV)
+        cases.append((it, xb, spear.spear_linear_decode(lay, x, workspace=ws)))
+    torch.cuda.synchronize()
+    for it, xb, y in cases:
+        assert_close(gpu_y_f64(y, "f16"), oracle_y(hl, xb), f"call {it}")
     assert spear.spear_workspace_flags(ws) == 0
     assert _ws_header(ws) == [0] * 11
 
