@@ -356,6 +356,45 @@ def llama70b_context(torch, device):
     return {"layer_copies": n_sets, "calls": out}
 
 
+def rank_gate_context(torch, device):
+    """The pages' per-rank gate (hidden 16, alpha 1) against the scalar gate and rank 0 on the
+    7B shapes: decode at M = 1 and 16 (fp16) and prefill at M = 2048 (bf16); layer copies rotate
+    over >= 1 GiB."""
+    from quantized_gemm_error_amd import spear, synth
+    w = synth.WORKLOADS["llama7b-decode"]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w["seed"] + 77)
+    out = {}
+    for K, N in w["shapes"]:
+        for M, act in ((1, torch.float16), (16, torch.float16), (2048, torch.bfloat16)):
+            base = random_layer(torch, N, K, w["group_size"], w["rank"], device, gen, act)
+            n_sets = max(2, -(-ROTATION_BYTES // layer_bytes(base)))
+            sets = [base] + [clone_layer(base) for _ in range(n_sets - 1)]
+            rg = spear.rank_gate_to_device(synth.make_rank_gate(w["rank"], 16, seed=K + N,
+                                                                 t_scale=0.01 * K ** 0.5), 1.0, device)
+            x = torch.randn((M, K), device=device, generator=gen).to(act)
+            y = torch.empty((M, N), dtype=act, device=device)
+            ws = spear.new_workspace(base, M)
+
+            def with_gate(l, gate):
+                return spear.SpearLayer(l.N, l.K, l.group_size, l.qweight, l.scales, l.zeros, l.rank,
+                                        l.A, l.B, l.w_gate, l.b_gate, gate)
+            t = {}
+            for name, mk in (("rank_gate", lambda l: with_gate(l, rg)), ("scalar_gate", lambda l: l),
+                             ("r0", lambda l: l.without_compensator())):
+                t[name] = graph_call_time_ms(
+                    torch, lambda i, s: spear.spear_linear(mk(sets[i % n_sets]), x, y=y, workspace=ws,
+                                                           main_stream=s), n_sets)
+            out[f"{K}->{N} M={M}"] = {
+                "us_rank_gate": round(t["rank_gate"] * 1e3, 2), "us_scalar_gate": round(t["scalar_gate"] * 1e3, 2),
+                "us_r0": round(t["r0"] * 1e3, 2),
+                "overhead_pct_rank_gate": round(100.0 * (t["rank_gate"] / t["r0"] - 1.0), 2),
+                "overhead_pct_scalar_gate": round(100.0 * (t["scalar_gate"] / t["r0"] - 1.0), 2)}
+            del sets, base, x, y, ws
+            torch.cuda.empty_cache()
+    return out
+
+
 def serving_context(torch, device):
     """Chunked serving over a 32-block stack of the three 7B projections (random-init g128
     4-bit, compensators of rank 32 on 4 seeded blocks).  A step is one prefill chunk of C
@@ -754,6 +793,8 @@ def main():
         extra["prefill_llama7b_bf16_M2048"] = prefill_context(torch, dev)
         log("llama-70B layer")
         extra["llama70b_layer_fp16"] = llama70b_context(torch, dev)
+        log("per-rank gate")
+        extra["rank_gate_7b"] = rank_gate_context(torch, dev)
         log("serving stack")
         extra["serving_stack_7b"] = serving_context(torch, dev)
         log("ceilings")
