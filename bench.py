@@ -2,6 +2,7 @@
 """Benchmark of the compensated 4-bit linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+    python bench.py --prefill-only      (the prefill calls alone, for profiling)
 
 Workload (the headline): Llama-7B-shaped decode projections 4096->4096,
 4096->11008 and 11008->4096 at M = 1, 4, 16 and 32 tokens; 4-bit weights
@@ -727,6 +728,9 @@ def main():
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from rocprofv3 CSV output (no GPU)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the Llama-7B prefill calls (M = 2048, bf16) and print them: "
+                         "the command that the prefill kernel profiles are taken with")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, out_dir=os.path.join(ROOT, "profiles"))
@@ -742,6 +746,10 @@ def main():
     spear.load_library()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+
+    if args.prefill_only:
+        print(json.dumps({"prefill_llama7b_bf16_M2048": prefill_context(torch, dev)}), flush=True)
+        return
 
     log("building decode workload")
     wl = DecodeWorkload(dev)

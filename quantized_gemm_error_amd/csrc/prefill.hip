@@ -85,6 +85,29 @@ constexpr int kEpiStr = kEpiRc + 4;  // LDS row stride of the chunk (floats)
 static_assert(BM * kEpiStr * 4 <= BM * LSTR * 2, "epilogue U chunk fits the activation tile");
 static_assert(BN * kEpiStr * 4 <= BN * LSTR * 2, "epilogue B chunk fits the weight tile");
 
+// Output tile of this workgroup.  Workgroups go to the eight XCDs in turn
+// (linear id mod 8) and each XCD has its own L2, so the tiles are renumbered:
+// each XCD's workgroups take one run of consecutive numbers, and numbers walk
+// the output in bands of kGroupM tile rows, column by column.  The
+// workgroups that one XCD holds at a time then cover a compact block of the
+// output and share its activation rows and weight columns in that L2.
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void gemm_tile(int &tm, int &tn) {
+  const int ntn = gridDim.x, ntm = gridDim.y;
+  const int T = ntn * ntm;
+  const int L = blockIdx.y * ntn + blockIdx.x;
+  const int c = L & 7;
+  int p = L >> 3;  // after the tiles of XCDs 0 .. c-1; XCD c' holds ceil((T - c') / 8)
+  for (int cc = 0; cc < c; ++cc) p += (T - cc + 7) >> 3;
+  const int per_group = kGroupM * ntn;
+  const int grp = p / per_group;
+  const int first = grp * kGroupM;
+  const int gsz = min(ntm - first, kGroupM);
+  const int r = p - grp * per_group;
+  tm = first + r % gsz;
+  tn = r / gsz;
+}
+
 template <int DT, bool PERCH, bool EPI, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
   static_assert(!(EPI && SPLIT), "split tiles are finished by prefill_finish_kernel");
@@ -96,7 +119,9 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, h = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  int tm, tn;
+  gemm_tile(tm, tn);
+  const int n0 = tn * BN, m0 = tm * BM;
   const int nkb = (a.K + BK - 1) / BK;
   const int kw = a.K / 8;
 
