@@ -215,22 +215,25 @@ def timed_decode_steps(torch, wl, steps, warmup):
     return total_ms, wall, cls_ms, classes
 
 
-def graph_call_time_ms(torch, issue_fn, n, reps=5):
-    """Average device time per call of n back-to-back calls captured in one graph."""
+def graph_times_ms(torch, variants, n, rounds=5, warm_ms=50.0):
+    """Average device time per call of each variant: n back-to-back calls captured in one
+    graph per variant.  The graphs are first replayed in turn until the GPU has been busy
+    for warm_ms (so that every variant runs at the same, settled clock), then timed in
+    alternation, `rounds` replays each; the best replay of each counts."""
     stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        for i in range(n):
-            issue_fn(i, stream)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(n):
-            issue_fn(i, stream)
-    with torch.cuda.stream(stream):
-        g.replay()
-    torch.cuda.synchronize()
-    best = None
-    for _ in range(reps):
+    graphs = {}
+    for name, issue_fn in variants.items():
+        with torch.cuda.stream(stream):
+            for i in range(n):
+                issue_fn(i, stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                issue_fn(i, stream)
+        graphs[name] = g
+
+    def timed(g):
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):   # replay() runs on the current stream
@@ -238,9 +241,25 @@ def graph_call_time_ms(torch, issue_fn, n, reps=5):
             g.replay()
             e.record(stream)
         torch.cuda.synchronize()
-        t = s.elapsed_time(e) / n
-        best = t if best is None else min(best, t)
+        return s.elapsed_time(e)
+
+    busy = 0.0
+    while busy < warm_ms:
+        for g in graphs.values():
+            busy += timed(g)
+    best = {}
+    names = list(graphs)
+    for r in range(rounds):
+        for k in range(len(names)):
+            name = names[(r + k) % len(names)]
+            t = timed(graphs[name]) / n
+            best[name] = t if name not in best else min(best[name], t)
     return best
+
+
+def graph_call_time_ms(torch, issue_fn, n, reps=5):
+    """Average device time per call of n back-to-back calls captured in one graph."""
+    return graph_times_ms(torch, {"v": issue_fn}, n, rounds=reps)["v"]
 
 
 def decode_overhead(torch, wl_ec, wl_r0):
@@ -248,8 +267,9 @@ def decode_overhead(torch, wl_ec, wl_r0):
     for si, (K, N) in enumerate(wl_ec.shapes):
         for M in wl_ec.tokens:
             n = wl_ec.n_sets
-            t_ec = graph_call_time_ms(torch, lambda i, s: wl_ec.issue(si, M, i % n, s), n)
-            t_r0 = graph_call_time_ms(torch, lambda i, s: wl_r0.issue(si, M, i % n, s), n)
+            t = graph_times_ms(torch, {"ec": lambda i, s: wl_ec.issue(si, M, i % n, s),
+                                       "r0": lambda i, s: wl_r0.issue(si, M, i % n, s)}, n)
+            t_ec, t_r0 = t["ec"], t["r0"]
             b = call_bytes(N, K, wl_ec.G, wl_ec.r, M)
             out[f"{K}->{N} M={M}"] = {
                 "us_ec": round(t_ec * 1e3, 3), "us_r0": round(t_r0 * 1e3, 3),
@@ -286,9 +306,8 @@ def prefill_context(torch, device):
 
         def run_r0(_i, s):
             spear.spear_linear_prefill(lay0, x, y=y, workspace=ws, main_stream=s)
-        t_s = graph_call_time_ms(torch, run_serial, 4)
-        t_c = graph_call_time_ms(torch, run_conc, 4)
-        t_r0 = graph_call_time_ms(torch, run_r0, 4)
+        t = graph_times_ms(torch, {"serial": run_serial, "conc": run_conc, "r0": run_r0}, 4)
+        t_s, t_c, t_r0 = t["serial"], t["conc"], t["r0"]
         f = call_flops(N, K, w["rank"], M)
         out[f"{K}->{N} M={M}"] = {
             "us_ec": round(t_s * 1e3, 1), "us_ec_concurrent": round(t_c * 1e3, 1),
@@ -337,12 +356,12 @@ def llama70b_context(torch, device):
             x = torch.randn((M, K), device=device, generator=gen).to(torch.float16)
             y = torch.empty((M, N), dtype=torch.float16, device=device)
             ws = spear.new_workspace(base[si], M)
-            t_ec = graph_call_time_ms(
-                torch, lambda i, s: spear.spear_linear(sets[i % n_sets][si], x, y=y, workspace=ws,
-                                                       main_stream=s), n_sets)
-            t_r0 = graph_call_time_ms(
-                torch, lambda i, s: spear.spear_linear(sets[i % n_sets][si].without_compensator(), x,
-                                                       y=y, workspace=ws, main_stream=s), n_sets)
+            t = graph_times_ms(torch, {
+                "ec": lambda i, s: spear.spear_linear(sets[i % n_sets][si], x, y=y, workspace=ws,
+                                                      main_stream=s),
+                "r0": lambda i, s: spear.spear_linear(sets[i % n_sets][si].without_compensator(), x,
+                                                      y=y, workspace=ws, main_stream=s)}, n_sets)
+            t_ec, t_r0 = t["ec"], t["r0"]
             b, f = call_bytes(N, K, K, r, M), call_flops(N, K, r, M)
             gbs, tfs = b / (t_ec * 1e-3) / 1e9, f / (t_ec * 1e-3) / 1e12
             out[f"{K}->{N} M={M}"] = {
@@ -380,12 +399,12 @@ def rank_gate_context(torch, device):
             def with_gate(l, gate):
                 return spear.SpearLayer(l.N, l.K, l.group_size, l.qweight, l.scales, l.zeros, l.rank,
                                         l.A, l.B, l.w_gate, l.b_gate, gate)
-            t = {}
-            for name, mk in (("rank_gate", lambda l: with_gate(l, rg)), ("scalar_gate", lambda l: l),
-                             ("r0", lambda l: l.without_compensator())):
-                t[name] = graph_call_time_ms(
-                    torch, lambda i, s: spear.spear_linear(mk(sets[i % n_sets]), x, y=y, workspace=ws,
-                                                           main_stream=s), n_sets)
+            def variant(mk):
+                return lambda i, s: spear.spear_linear(mk(sets[i % n_sets]), x, y=y, workspace=ws,
+                                                       main_stream=s)
+            t = graph_times_ms(torch, {"rank_gate": variant(lambda l: with_gate(l, rg)),
+                                       "scalar_gate": variant(lambda l: l),
+                                       "r0": variant(lambda l: l.without_compensator())}, n_sets)
             out[f"{K}->{N} M={M}"] = {
                 "us_rank_gate": round(t["rank_gate"] * 1e3, 2), "us_scalar_gate": round(t["scalar_gate"] * 1e3, 2),
                 "us_r0": round(t["r0"] * 1e3, 2),

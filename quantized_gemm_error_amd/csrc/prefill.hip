@@ -7,8 +7,11 @@
 //
 //  * prefill_ec_kernel computes the sums [A; w_g] x per token (rows 0..rank,
 //    the last being the gate's pre-activation z) into the workspace, with K
-//    split over up to four workgroups per 32 tokens; each split stores its
-//    own partial sums;
+//    split over several workgroups per 32 tokens; each split stores its own
+//    partial sums;
+//  * prefill_u_kernel (or, with the per-rank gate, prefill_rgate_kernel)
+//    forms U = diag(g) (X A^T) once from those partials: g = sigmoid(z + b_g),
+//    each sum taken in split order;
 //  * prefill_gemm_kernel, a 128x128x128-tiled MFMA GEMM.  Each k-block stages
 //    the activation tile and the exactly dequantized weight tile (q - z in
 //    the activation type) in LDS; four waves each own a 64x64 quarter of the
@@ -20,10 +23,8 @@
 //    split partials (with the per-channel scale) or the rounded y of the
 //    concurrent schedule, plus U B^T, rounded once into y.
 //
-// Whoever needs U = diag(g) (X A^T) forms it from the compensator's split
-// partials, summed in split order: g = sigmoid(z + b_g).  Every reduction
-// across workgroups happens across a kernel boundary, so no kernel here
-// waits on another workgroup.
+// Every reduction across workgroups happens across a kernel boundary, so no
+// kernel here waits on another workgroup.
 //
 // Schedules:
 //  * serial (no aux stream): compensator, then the GEMM, whose epilogue adds
@@ -46,26 +47,31 @@ namespace {
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int LSTR = BK + 8;  // LDS row stride (halves), padded against bank conflicts
 
-// The compensator's split partials: Tp[q][m][j], j = 0..rank (j = rank: z).
-struct EcView {
-  const float *Tp;
-  int ks, M, rank, rp1;
-  float b_gate;
+// U = diag(g) (X A^T) as the consumers read it: U[m][j] for j < rank and
+// zeros in columns rank .. rp1-1 (rp1 a multiple of 4), so that every 16-byte
+// piece of a row can be read whole.
+struct UView {
+  const float *U;  // [M][rp1]
+  int M, rank, rp1;
 };
 
-// Sum of token m's split partials of row j, in split order.
-__device__ __forceinline__ float ec_sum(const EcView &e, int m, int j) {
-  float t = 0.f;
-  for (int q = 0; q < e.ks; ++q) t += e.Tp[((size_t)q * e.M + m) * e.rp1 + j];
-  return t;
+// Four consecutive columns j..j+3 of row m, zeros for rows past M or columns
+// past the row.  The load itself is always made (from a clamped, valid
+// address) and the zeros selected afterwards, so that a batch of these loads
+// has no branches and stays in flight together.
+__device__ __forceinline__ f32x4_t u_piece(const UView &u, int m, int j) {
+  const bool in = m < u.M && j < u.rp1;
+  const f32x4_t v =
+      *(const f32x4_t *)(u.U + (size_t)min(m, u.M - 1) * u.rp1 + min(j, u.rp1 - 4));
+  return in ? v : f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-// Four consecutive rows j..j+3 of token m (rp1 is a multiple of 4, so the
-// four values are one 16-byte piece of each split's row).
-__device__ __forceinline__ f32x4_t ec_sum4(const EcView &e, int m, int j) {
-  f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-  for (int q = 0; q < e.ks; ++q) t += *(const f32x4_t *)(e.Tp + ((size_t)q * e.M + m) * e.rp1 + j);
-  return t;
+// Round to bf16 and the bf16 of the remainder: hi + lo equals v to a relative
+// 2^-16 (exactly when v has at most 16 significant bits, as fp16 values do).
+__device__ __forceinline__ void split_bf16(float v, uint16_t &hi, uint16_t &lo) {
+  const __bf16 h = (__bf16)v;
+  hi = bitcast<uint16_t>(h);
+  lo = bitcast<uint16_t>((__bf16)(v - (float)h));
 }
 
 struct GemmArgs {
@@ -74,16 +80,16 @@ struct GemmArgs {
   const uint16_t *x;
   uint16_t *y;
   int N, K, G, ngroups, M;
-  EcView ec;          // EPI: the compensator's partials, complete before the launch
+  UView u;            // EPI: U, complete before the launch
   const uint16_t *B;  // EPI: [N][rank]
   int ks;             // SPLIT: K splits (blockIdx.z), each a contiguous range of k-blocks
   float *part;        // SPLIT: [ks][M][N] fp32 partial outputs
 };
 
-constexpr int kEpiRc = 32;           // ranks per epilogue chunk
-constexpr int kEpiStr = kEpiRc + 4;  // LDS row stride of the chunk (floats)
-static_assert(BM * kEpiStr * 4 <= BM * LSTR * 2, "epilogue U chunk fits the activation tile");
-static_assert(BN * kEpiStr * 4 <= BN * LSTR * 2, "epilogue B chunk fits the weight tile");
+constexpr int kEpiRc = 32;           // ranks per epilogue chunk: the K of one 16x16x32 MFMA
+constexpr int kEpiStr = kEpiRc + 8;  // LDS row stride of a chunk's bf16 operands (halves)
+static_assert(2 * BM * kEpiStr <= BM * LSTR, "epilogue U hi/lo fit the activation tile");
+static_assert(2 * BN * kEpiStr <= BN * LSTR, "epilogue B hi/lo fit the weight tile");
 
 // Output tile of this workgroup.  Workgroups go to the eight XCDs in turn
 // (linear id mod 8) and each XCD has its own L2, so the tiles are renumbered:
@@ -114,7 +120,6 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
   __shared__ __align__(16) uint16_t xs[BM * LSTR];
   __shared__ __align__(16) uint16_t wsm[BN * LSTR];
   __shared__ float ss[BN];
-  __shared__ float gs[BM];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, h = lane >> 4;
@@ -178,20 +183,8 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // this workgroup's k-blocks: all of them, or split blockIdx.z of ks
-  int kb_lo = 0, kb_hi = nkb;
-  if constexpr (SPLIT) {
-    const int per = (nkb + a.ks - 1) / a.ks;
-    kb_lo = min(nkb, (int)blockIdx.z * per);
-    kb_hi = min(nkb, kb_lo + per);
-  }
-  if (kb_lo < kb_hi) gload(kb_lo);
-  for (int kb = kb_lo; kb < kb_hi; ++kb) {
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (kb + 1 < kb_hi) gload(kb + 1);
-
+  // one k-block from the staged tiles
+  auto compute = [&]() {
     u32x4_t af[4][4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
@@ -221,6 +214,63 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
         }
       }
     }
+  };
+
+  // EPI operands of one rank chunk: this thread's 4 pieces of U (4 ranks of
+  // a row each) and, when r % 8 == 0 and B is 16-byte aligned, its 2 pieces of
+  // B (8 ranks of a row each).  epi_load reads them raw from clamped, valid
+  // addresses; epi_value selects zeros for rows past M or N and ranks past r
+  // when they are staged.  The first chunk is loaded during the last k-block,
+  // and as nothing reads the registers before the staging, the loads stay in
+  // flight behind that block's MFMAs.
+  f32x4_t u_pre[4];
+  u16x8_t b_pre[2];
+  const bool bvec = (a.u.rank % 8) == 0 && ((uintptr_t)a.B % 16) == 0;
+  auto epi_load = [&](int j0) {
+    const UView &u = a.u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid + 256 * i;  // BM rows x 8 pieces
+      const int r = p >> 3, j = j0 + 4 * (p & 7);
+      u_pre[i] = *(const f32x4_t *)(u.U + (size_t)min(m0 + r, a.M - 1) * u.rp1 + min(j, u.rp1 - 4));
+    }
+    if (bvec) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int p = tid + 256 * i;  // BN rows x 4 pieces of 8 ranks
+        const int r = p >> 2, j = j0 + 8 * (p & 3);
+        b_pre[i] = *(const u16x8_t *)(a.B + (size_t)min(n0 + r, a.N - 1) * u.rank + min(j, u.rank - 8));
+      }
+    }
+  };
+
+  // this workgroup's k-blocks: all of them, or split blockIdx.z of ks; the
+  // last one is peeled off, as it loads the epilogue's operands instead of a
+  // next block
+  int kb_lo = 0, kb_hi = nkb;
+  if constexpr (SPLIT) {
+    const int per = (nkb + a.ks - 1) / a.ks;
+    kb_lo = min(nkb, (int)blockIdx.z * per);
+    kb_hi = min(nkb, kb_lo + per);
+  }
+  if (kb_lo < kb_hi) gload(kb_lo);
+  for (int kb = kb_lo; kb + 1 < kb_hi; ++kb) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    gload(kb + 1);
+    compute();
+  }
+  if (kb_lo < kb_hi) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if constexpr (EPI) {
+      if (a.u.rank > 0) epi_load(0);
+    }
+    compute();
+  } else if constexpr (EPI) {
+    if (a.u.rank > 0) epi_load(0);
   }
 
   if constexpr (SPLIT) {
@@ -251,49 +301,75 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
   }
 
   if constexpr (EPI) {
-    // y tile += U[m0.., :] B[n0.., :]^T with U = g * T formed from the
-    // compensator's split partials; kEpiRc ranks at a time staged in the (now
-    // free) LDS tiles; rows past M or N and ranks past r stage zeros
-    const EcView &e = a.ec;
-    __syncthreads();  // the tiles' last readers are done
-    if (tid < BM) gs[tid] = (m0 + tid < a.M) ? gate_sigmoid(ec_sum(e, m0 + tid, e.rank) + e.b_gate) : 0.f;
-    float *us = (float *)xs;
-    float *bs = (float *)wsm;
-    const int uq = kEpiRc / 4;
-    for (int j0 = 0; j0 < e.rank; j0 += kEpiRc) {
-      __syncthreads();  // gs written / the previous chunk's readers are done
+    // y tile += U[m0.., :] B[n0.., :]^T, kEpiRc ranks at a time staged in the
+    // (now free) LDS tiles as bf16 pairs: hi = the value rounded to bf16, lo =
+    // the remainder rounded to bf16.  U hi and lo times B (hi and lo when B is
+    // fp16, which the pair holds exactly) in 16x16x32 bf16 MFMAs with fp32
+    // accumulation give U B^T to a relative 2^-16.  Rows past M or N and
+    // ranks past r stage zeros.
+    const UView &u = a.u;
+    uint16_t *uh = xs, *ul = xs + BM * kEpiStr;
+    uint16_t *bh = wsm, *bl = wsm + BN * kEpiStr;
+    for (int j0 = 0; j0 < u.rank; j0 += kEpiRc) {
+      if (j0 > 0) epi_load(j0);
+      __syncthreads();  // the tiles' (or the previous chunk's) last readers are done
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int p = tid + 256 * i;  // BM rows x uq pieces
-        const int r = p / uq, q = p - r * uq;
-        const int j = j0 + 4 * q;
-        f32x4_t u = {0.f, 0.f, 0.f, 0.f};
-        if (m0 + r < a.M && j < e.rp1) u = gs[r] * ec_sum4(e, m0 + r, j);
+        const int p = tid + 256 * i;
+        const int r = p >> 3, q = p & 7;
+        const bool in = m0 + r < a.M && j0 + 4 * q < u.rp1;
+        uint16_t hv[4], lv[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (j + c >= e.rank) u[c] = 0.f;
-        *(f32x4_t *)(us + r * kEpiStr + 4 * q) = u;
+        for (int c = 0; c < 4; ++c) split_bf16(in ? u_pre[i][c] : 0.f, hv[c], lv[c]);
+        *(uint2 *)(uh + r * kEpiStr + 4 * q) =
+            uint2{hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16)};
+        *(uint2 *)(ul + r * kEpiStr + 4 * q) =
+            uint2{lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16)};
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int p = tid + 256 * i;  // BN rows x kEpiRc ranks
-        const int r = p / kEpiRc, jj = p - r * kEpiRc;
-        bs[r * kEpiStr + jj] = (n0 + r < a.N && j0 + jj < e.rank)
-                                   ? to_f32<DT>(a.B[(size_t)(n0 + r) * e.rank + j0 + jj]) : 0.f;
+        // value i of this thread: rank jj of row r (two 8-rank pieces when
+        // prefetched, else one value per row-rank slot, loaded now)
+        int r, jj;
+        uint16_t v;
+        if (bvec) {
+          const int p = tid + 256 * (i >> 3);
+          r = p >> 2;
+          jj = 8 * (p & 3) + (i & 7);
+          v = b_pre[i >> 3][i & 7];
+        } else {
+          const int p = tid + 256 * i;
+          r = p / kEpiRc;
+          jj = p - r * kEpiRc;
+          v = a.B[(size_t)min(n0 + r, a.N - 1) * u.rank + min(j0 + jj, u.rank - 1)];
+        }
+        if (n0 + r >= a.N || j0 + jj >= u.rank) v = 0;
+        if constexpr (DT == DT_BF16) {
+          bh[r * kEpiStr + jj] = v;
+        } else {
+          uint16_t hv, lv;
+          split_bf16(to_f32<DT>(v), hv, lv);
+          bh[r * kEpiStr + jj] = hv;
+          bl[r * kEpiStr + jj] = lv;
+        }
       }
       __syncthreads();
 #pragma unroll
-      for (int st = 0; st < kEpiRc / 4; ++st) {
-        const int j = 4 * st + h;
-        float ua[4], ba[4];
+      for (int mi = 0; mi < 4; ++mi) {
+        const int ro = (64 * wm + 16 * mi + col) * kEpiStr + 8 * h;
+        const u32x4_t ah = *(const u32x4_t *)(uh + ro);
+        const u32x4_t al = *(const u32x4_t *)(ul + ro);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) ua[mi] = us[(64 * wm + 16 * mi + col) * kEpiStr + j];
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) ba[ni] = bs[(64 * wn + 16 * ni + col) * kEpiStr + j];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_16x16x4_f32(ua[mi], ba[ni], acc[mi][ni]);
+        for (int ni = 0; ni < 4; ++ni) {
+          const int co = (64 * wn + 16 * ni + col) * kEpiStr + 8 * h;
+          const u32x4_t b0 = *(const u32x4_t *)(bh + co);
+          acc[mi][ni] = mfma_16x16x32<DT_BF16>(ah, b0, acc[mi][ni]);
+          acc[mi][ni] = mfma_16x16x32<DT_BF16>(al, b0, acc[mi][ni]);
+          if constexpr (DT == DT_F16) {
+            const u32x4_t b1 = *(const u32x4_t *)(bl + co);
+            acc[mi][ni] = mfma_16x16x32<DT_BF16>(ah, b1, acc[mi][ni]);
+          }
+        }
       }
     }
   }
@@ -429,12 +505,11 @@ __global__ __launch_bounds__(64 * kEcWaves) void prefill_ec_kernel(EcArgs a) {
 
 // The pages' per-rank gate: for each token, t = the sum of its split
 // partials (rows 0..rank-1, split order), hidden = relu(W1 t + b1),
-// gamma = sigmoid(W2 hidden + b2), and Ts[m][j] = alpha gamma_j t_j.  Column
-// rank of Ts is set to +infinity, so that consumers, which apply the scalar
-// gate sigmoid(Ts[m][rank] + 0), multiply by exactly 1.
+// gamma = sigmoid(W2 hidden + b2), and U[m][j] = alpha gamma_j t_j, with
+// zeros in columns rank .. rp1-1.
 struct RgArgs {
   const float *Tp;
-  float *Ts;  // [M][rp1]
+  float *Ts;  // U: [M][rp1]
   int ks, M, rank, rp1, hidden;
   const float *W1, *b1, *W2, *b2;
   float alpha;
@@ -469,26 +544,40 @@ __global__ __launch_bounds__(256) void prefill_rgate_kernel(RgArgs a) {
     for (int c = 0; c < a.hidden; ++c) v += a.W2[(size_t)j * a.hidden + c] * hl[mm][c];
     a.Ts[(size_t)m * a.rp1 + j] = a.alpha * gate_sigmoid(v) * tl[mm][j];
   }
-  if (tid < kRgTok && m0 + tid < a.M) a.Ts[(size_t)(m0 + tid) * a.rp1 + a.rank] = __builtin_inff();
+  for (int i = tid; i < kRgTok * (a.rp1 - a.rank); i += 256) {
+    const int mm = i / (a.rp1 - a.rank), j = a.rank + i - mm * (a.rp1 - a.rank);
+    if (m0 + mm < a.M) a.Ts[(size_t)(m0 + mm) * a.rp1 + j] = 0.f;
+  }
 }
 
-// Sum of the compensator's split partials, Ts[m][j] = sum_q Tp[q][m][j] in
-// split order, for the many-split case (few tokens): consumers then read one
-// partial per value.
-struct EcSumArgs {
+// U = diag(g) (X A^T) from the compensator's split partials: for token m,
+// t_j = sum_q Tp[q][m][j] (j < rank) and z = the same sum of row rank, each
+// in split order; g = sigmoid(z + b_g); U[m][j] = g t_j, and zeros in
+// columns rank .. rp1-1.  One thread per 4-column piece.
+struct UArgs {
   const float *Tp;
-  float *Ts;  // [M][rp1]
+  float *U;  // [M][rp1]
   int ks, M, rank, rp1;
+  float b_gate;
 };
 
-__global__ __launch_bounds__(256) void prefill_ec_sum_kernel(EcSumArgs a) {
+__global__ __launch_bounds__(256) void prefill_u_kernel(UArgs a) {
+  const int q4 = a.rp1 / 4;
   const int i = blockIdx.x * 256 + threadIdx.x;
-  const int n = a.M * (a.rank + 1);
-  if (i >= n) return;
-  const int m = i / (a.rank + 1), j = i - m * (a.rank + 1);
-  float t = 0.f;
-  for (int q = 0; q < a.ks; ++q) t += a.Tp[((size_t)q * a.M + m) * a.rp1 + j];
-  a.Ts[(size_t)m * a.rp1 + j] = t;
+  if (i >= a.M * q4) return;
+  const int m = i / q4, j = 4 * (i - m * q4);
+  f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+  float z = 0.f;
+  for (int q = 0; q < a.ks; ++q) {
+    const float *row = a.Tp + ((size_t)q * a.M + m) * a.rp1;
+    t += *(const f32x4_t *)(row + j);
+    z += row[a.rank];
+  }
+  const float g = gate_sigmoid(z + a.b_gate);
+  f32x4_t u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) u[c] = (j + c < a.rank) ? g * t[c] : 0.f;
+  *(f32x4_t *)(a.U + (size_t)m * a.rp1 + j) = u;
 }
 
 // ---------------------------------------------------------------------------
@@ -497,8 +586,8 @@ __global__ __launch_bounds__(256) void prefill_ec_sum_kernel(EcSumArgs a) {
 // where base is the sum of the GEMM's split partials in split order (times
 // the row's scale when one scale covers the row) or, in the concurrent
 // schedule, the GEMM's rounded y; the U B^T term is present when the layer
-// has a compensator.  The base tile, the U rows (formed from the
-// compensator's partials) and the B rows are staged in LDS; four waves each
+// has a compensator.  The base tile, the U rows and the B rows are staged in
+// LDS; four waves each
 // take 16 tokens with fp32 16x16x4 MFMAs; y goes back in 16-byte stores when
 // its rows are 16-byte aligned.
 // ---------------------------------------------------------------------------
@@ -507,7 +596,7 @@ struct FinishArgs {
   const float *part;  // PARTS: [ks][M][N]
   int ks;
   const uint16_t *scales;  // PARTS && PERCH: [N]
-  EcView ec;               // EC
+  UView u;                 // EC
   const uint16_t *B;       // EC: [N][rank]
   int N, M;
 };
@@ -522,7 +611,6 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(FinishArgs a) {
   __shared__ __align__(16) float ts[kFT][kFStr];
   __shared__ __align__(16) float us[kFT][kFRStr];
   __shared__ __align__(16) float bs[kFT][kFRStr];
-  __shared__ float gs[kFT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, h = lane >> 4;
   const int n0 = blockIdx.x * kFT, m0 = blockIdx.y * kFT;
@@ -562,21 +650,14 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(FinishArgs a) {
   }
 
   if constexpr (EC) {
-    const EcView &e = a.ec;
-    if (tid < kFT) gs[tid] = (m0 + tid < a.M) ? gate_sigmoid(ec_sum(e, m0 + tid, e.rank) + e.b_gate) : 0.f;
+    const UView &e = a.u;
     for (int j0 = 0; j0 < e.rank; j0 += kFRc) {
-      __syncthreads();  // gs / base tile written; the previous chunk's readers are done
+      __syncthreads();  // base tile written; the previous chunk's readers are done
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int p = tid + 256 * i;  // 64 rows x 8 pieces
         const int r = p >> 3, q = p & 7;
-        const int j = j0 + 4 * q;
-        f32x4_t u = {0.f, 0.f, 0.f, 0.f};
-        if (m0 + r < a.M && j < e.rp1) u = gs[r] * ec_sum4(e, m0 + r, j);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (j + c >= e.rank) u[c] = 0.f;
-        *(f32x4_t *)&us[r][4 * q] = u;
+        *(f32x4_t *)&us[r][4 * q] = u_piece(e, m0 + r, j0 + 4 * q);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -653,10 +734,8 @@ static int rank_pad(int rank) { return (rank + 3) / 4 * 4; }
 static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Compensator K splits: about 256 workgroups of 32 tokens, at least one
-// 32-wide step per wave, at most 64.  Up to kEcDirectKs splits the consumers
-// of U sum them directly; beyond that prefill_ec_sum_kernel sums them once.
-// ks * ceil(M / 32) <= 256 + ceil(M / 32) bounds the partials.
-constexpr int kEcDirectKs = 4;
+// 32-wide step per wave, at most 64.  ks * ceil(M / 32) <= 256 + ceil(M / 32)
+// bounds the partials.
 static int ec_ksplit(int M, int K) {
   const int nblk = (M + kEcTok - 1) / kEcTok;
   int ks = (256 + nblk - 1) / nblk;
@@ -683,7 +762,7 @@ static int gemm_ksplit(int M, int N, int K) {
 }
 
 // Workspace layout after the 2048-byte header: the compensator's split
-// partials [ks][M][rp1], their sum [M][rp1] (many splits only) and the GEMM's
+// partials [ks][M][rp1], U [M][rp1] formed from them, and the GEMM's
 // split partials (at most kGemmSplitWgs tiles of 128 x 128 fp32).  All are
 // rewritten in full by every call before they are read and are sized by
 // bounds that grow with M, so a workspace for M serves every call with fewer
@@ -736,7 +815,7 @@ hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint
   const bool concurrent = ec && aux_s != nullptr && aux_s != main_s;
   const PrefillWs w = prefill_ws_layout(L, M);
   char *base = (char *)ws;
-  EcView ev{};
+  UView uv{};
   EcArgs ea{};
   int eks = 1;
   const bool rgate = ec && L.rg_hidden > 0;
@@ -744,21 +823,18 @@ hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint
     const int rp1 = rank_pad(L.rank + 1);
     eks = ec_ksplit(M, L.K);
     ea = EcArgs{x, L.A, L.wg, L.K, M, L.rank, L.rank + L.gate_rows(), rp1, eks, (float *)(base + w.tp)};
-    // consumers read the split partials directly, or their one-time sum (or,
-    // with the per-rank gate, the gated U with a gate column of +infinity)
-    ev = (eks <= kEcDirectKs && !rgate)
-             ? EcView{(const float *)(base + w.tp), eks, M, L.rank, rp1, L.b_gate}
-             : EcView{(const float *)(base + w.ts), 1, M, L.rank, rp1, rgate ? 0.f : L.b_gate};
+    // consumers read U, formed once from the split partials
+    uv = UView{(const float *)(base + w.ts), M, L.rank, rp1};
   }
   // split K only with a workspace (a rank-0 call may come without one)
   const int gks = ws ? gemm_ksplit(M, L.N, L.K) : 1;
   const bool split = gks > 1;
-  GemmArgs g{L.qw, L.scales, L.zeros, x, y, L.N, L.K, L.G, L.ngroups, M, ev, L.B, gks,
+  GemmArgs g{L.qw, L.scales, L.zeros, x, y, L.N, L.K, L.G, L.ngroups, M, uv, L.B, gks,
              split ? (float *)(base + w.gpart) : nullptr};
   const dim3 ggrid((L.N + BN - 1) / BN, (M + BM - 1) / BM, gks);
   const dim3 egrid(((M + kEcTok - 1) / kEcTok) * eks);
   const dim3 fgrid((L.N + kFT - 1) / kFT, (M + kFT - 1) / kFT);
-  FinishArgs fa{y, g.part, gks, L.scales, ev, L.B, L.N, M};
+  FinishArgs fa{y, g.part, gks, L.scales, uv, L.B, L.N, M};
   hipError_t e = hipSuccess;
 
   auto launch_ec = [&](hipStream_t s) {
@@ -774,10 +850,9 @@ hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint
       hipLaunchKernelGGL(prefill_rgate_kernel, dim3((M + kRgTok - 1) / kRgTok), dim3(256), 0, s, ra);
       return hipGetLastError();
     }
-    if (eks <= kEcDirectKs) return r;
-    const EcSumArgs sa{ea.Tp, (float *)(base + w.ts), eks, M, L.rank, ea.rp1};
-    const int n = M * (L.rank + 1);
-    hipLaunchKernelGGL(prefill_ec_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, s, sa);
+    const UArgs ua{ea.Tp, (float *)(base + w.ts), eks, M, L.rank, ea.rp1, L.b_gate};
+    const int n = M * (ea.rp1 / 4);
+    hipLaunchKernelGGL(prefill_u_kernel, dim3((n + 255) / 256), dim3(256), 0, s, ua);
     return hipGetLastError();
   };
   // the GEMM, then (split) the finish kernel over the partials; `epi` adds
