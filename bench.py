@@ -735,6 +735,97 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
     print(json.dumps(rec))
 
 
+PREFILL_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_prefill_trace -o run -- "
+                     "python3 bench.py --prefill-only")
+PREFILL_PMC = (("pmc1", "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+                        "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAVE_CYCLES GRBM_GUI_ACTIVE"),
+               ("pmc2", "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY SQ_WAIT_INST_LDS SQ_WAIT_ANY "
+                        "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_LDS_DATA_FIFO_FULL SQ_VALU_MFMA_COEXEC_CYCLES "
+                        "GRBM_GUI_ACTIVE"))
+PREFILL_PMC_CMD = ("rocprofv3 --pmc {counters} -f csv -d gpurun_out/prof_prefill_{tag} -o run -- "
+                   "python3 bench.py --prefill-only")
+
+
+def summarize_prefill_profiles(trace_dir, pmc1_dir, pmc2_dir, out_dir):
+    """profiles/prefill_kernels_llama7b_m2048.md from the prefill-only trace and counter passes."""
+    import csv
+    import re
+    import statistics
+
+    def rows(path):
+        with open(path, newline="") as f:
+            return list(csv.DictReader(f))
+
+    def short(name):
+        m = re.search(r"(prefill_\w+)(<[^>]*>)?", name)
+        return (m.group(1) + (m.group(2) or "")) if m else name.split("(")[0][:60]
+
+    trace = [r for r in rows(os.path.join(trace_dir, "run_kernel_trace.csv")) if "prefill_" in r["Kernel_Name"]]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    # the calls run shape by shape (4096->4096, 4096->11008, 11008->4096); the 86-tile
+    # grid of the GEMM marks the middle shape
+    n_of = lambda r: int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+    mid = [i for i, r in enumerate(trace) if "gemm" in r["Kernel_Name"] and n_of(r) == 86]
+    lo = mid[0]
+    while lo > 0 and "gemm" not in trace[lo - 1]["Kernel_Name"]:
+        lo -= 1
+    parts = {"4096->4096": trace[:lo], "4096->11008": trace[lo:mid[-1] + 1], "11008->4096": trace[mid[-1] + 1:]}
+    lines = ["# Prefill kernels, Llama-7B projections at M = 2048 (bf16): rocprofv3 trace and counters", "",
+             "Commands (repository root, one MI355X):", "", "    " + PREFILL_TRACE_CMD]
+    for tag, counters in PREFILL_PMC:
+        lines.append("    " + PREFILL_PMC_CMD.format(counters=counters, tag=tag))
+    lines += ["", "`bench.py --prefill-only` runs, per shape, the serial schedule (compensator, U, "
+                  "then the GEMM with U B^T in its epilogue), the concurrent schedule and rank 0, "
+                  "each as graph replays.  rocprofv3 stamps a kernel's start when the previous one "
+                  "in the stream ends, so durations are launch to launch.", "",
+              "Median duration per kernel and shape (us):", "",
+              "| shape | kernel | dispatches | median us |", "|---|---|---:|---:|"]
+    for shape, rs in parts.items():
+        per = {}
+        for r in rs:
+            per.setdefault(short(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for k, v in per.items():
+            lines.append(f"| {shape} | `{k}` | {len(v)} | {statistics.median(v):.1f} |")
+
+    def pmc(d):
+        per = {}
+        for r in rows(os.path.join(d, "run_counter_collection.csv")):
+            if "prefill_" not in r["Kernel_Name"]:
+                continue
+            per.setdefault(short(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        return {k: {c: statistics.mean(v) for c, v in cs.items()} for k, cs in per.items()}
+
+    c1, c2 = pmc(pmc1_dir), pmc(pmc2_dir)
+    lines += ["", "Counters per dispatch, mean over the dispatches of each kernel (all three shapes). "
+                  "GRBM_GUI_ACTIVE is summed over the 8 XCDs, so one XCD's busy cycles are an "
+                  "eighth of it; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x "
+                  "1024 SIMDs).", "",
+              "| kernel | MFMA busy | VALU instr per MFMA | LDS bank-conflict cycles / LDS active | "
+              "MFMA cycles with VALU co-issue | LDS wait / all wait |",
+              "|---|---:|---:|---:|---:|---:|"]
+    for k in sorted(c1):
+        a, b = c1[k], c2.get(k, {})
+        xcd = a["GRBM_GUI_ACTIVE"] / 8.0
+        busy = a["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd * 1024) if xcd else 0.0
+        vpm = a["SQ_INSTS_VALU"] / a["SQ_INSTS_MFMA"] if a.get("SQ_INSTS_MFMA") else float("nan")
+        bank = a["SQ_LDS_BANK_CONFLICT"] / a["SQ_LDS_IDX_ACTIVE"] if a.get("SQ_LDS_IDX_ACTIVE") else 0.0
+        co = (b.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / a["SQ_VALU_MFMA_BUSY_CYCLES"]
+              if a.get("SQ_VALU_MFMA_BUSY_CYCLES") else 0.0)
+        lw = b.get("SQ_WAIT_INST_LDS", 0.0) / b["SQ_WAIT_ANY"] if b.get("SQ_WAIT_ANY") else 0.0
+        vpm_s = f"{vpm:.2f}" if vpm == vpm else "-"
+        lines.append(f"| `{k}` | {100 * busy:.1f}% | {vpm_s} | {100 * bank:.1f}% | {100 * co:.1f}% | "
+                     f"{100 * lw:.1f}% |")
+    lines += ["", "Raw means per dispatch:", "", "| kernel | counter | value |", "|---|---|---:|"]
+    for k in sorted(c1):
+        for c, v in sorted({**c1[k], **c2.get(k, {})}.items()):
+            lines.append(f"| `{k}` | {c} | {v:.4g} |")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "prefill_kernels_llama7b_m2048.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -747,12 +838,17 @@ def main():
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from rocprofv3 CSV output (no GPU)")
+    ap.add_argument("--summarize-prefill-profiles", nargs=3, metavar=("TRACE_DIR", "PMC1_DIR", "PMC2_DIR"),
+                    help="write the prefill profile summary from rocprofv3 CSV output (no GPU)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the Llama-7B prefill calls (M = 2048, bf16) and print them: "
                          "the command that the prefill kernel profiles are taken with")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, out_dir=os.path.join(ROOT, "profiles"))
+        return
+    if args.summarize_prefill_profiles:
+        summarize_prefill_profiles(*args.summarize_prefill_profiles, out_dir=os.path.join(ROOT, "profiles"))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
