@@ -263,16 +263,28 @@ def graph_call_time_ms(torch, issue_fn, n, reps=5):
 
 
 def decode_overhead(torch, wl_ec, wl_r0):
+    """Per shape and M: the fused decode call with the compensator, the same kernel at rank 0,
+    and the unfused form of the same call (the prefill path at decode M: the compensator
+    kernel, U, the split-K GEMM and the kernel that adds U B^T, four launches), which is the
+    pages' naive-insertion comparison."""
+    from quantized_gemm_error_amd import spear
     out = {}
     for si, (K, N) in enumerate(wl_ec.shapes):
         for M in wl_ec.tokens:
             n = wl_ec.n_sets
+
+            def unfused(i, s):
+                spear.spear_linear_prefill(wl_ec.sets[i % n][si], wl_ec.x[(K, M)], y=wl_ec.y[(N, M)],
+                                           workspace=wl_ec.ws[si], main_stream=s)
             t = graph_times_ms(torch, {"ec": lambda i, s: wl_ec.issue(si, M, i % n, s),
-                                       "r0": lambda i, s: wl_r0.issue(si, M, i % n, s)}, n)
+                                       "r0": lambda i, s: wl_r0.issue(si, M, i % n, s),
+                                       "unfused": unfused}, n)
             t_ec, t_r0 = t["ec"], t["r0"]
             b = call_bytes(N, K, wl_ec.G, wl_ec.r, M)
             out[f"{K}->{N} M={M}"] = {
                 "us_ec": round(t_ec * 1e3, 3), "us_r0": round(t_r0 * 1e3, 3),
+                "us_unfused": round(t["unfused"] * 1e3, 3),
+                "unfused_over_fused": round(t["unfused"] / t_ec, 3),
                 "overhead_pct": round(100.0 * (t_ec / t_r0 - 1.0), 2),
                 "GBps_ec": round(b / (t_ec * 1e-3) / 1e9, 1),
                 "hbm_frac_ec": round(b / (t_ec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -417,68 +429,79 @@ def rank_gate_context(torch, device):
 
 def serving_context(torch, device):
     """Chunked serving over a 32-block stack of the three 7B projections (random-init g128
-    4-bit, compensators of rank 32 on 4 seeded blocks).  A step is one prefill chunk of C
-    tokens plus 32 decode tokens through every linear.  A latency table measured per
-    (shape, compensated or not, C or decode) predicts the step time; the chunk selector
-    picks C for each budget; the chosen step is then run and timed."""
+    4-bit; every block carries a rank-32 compensator, and a density d switches on those of d
+    seeded blocks).  A step is one prefill chunk of C tokens plus 32 decode tokens through
+    every linear.  A latency table measured per (shape, compensated or not, C or decode)
+    predicts the step time at every density; the chunk selector picks C for each budget.  At
+    the configured density (4 blocks) every budget's chosen step is run and timed; at the
+    other densities (0, 8, 16, 32) the step chosen for a 16 ms budget is."""
     from quantized_gemm_error_amd import spear, synth
     w = synth.WORKLOADS["llama7b-stack-serving"]
     gen = torch.Generator(device=device)
     gen.manual_seed(w["seed"])
     shapes, chunks, n_dec = list(w["shapes"]), list(w["chunks"]), w["decode_tokens"]
-    ec_set = {int(b) for b in synth.ec_block_indices(w["blocks"], w["ec_blocks"], w["seed"])}
-    stack = [[random_layer(torch, N, K, w["group_size"], w["rank"] if b in ec_set else 0, device, gen,
-                           torch.float16) for K, N in shapes] for b in range(w["blocks"])]
+    nb = w["blocks"]
+    stack = [[random_layer(torch, N, K, w["group_size"], w["rank"], device, gen, torch.float16)
+              for K, N in shapes] for b in range(nb)]
+    plain = [[l.without_compensator() for l in blk] for blk in stack]
+    densities = (0, w["ec_blocks"], 8, 16, nb)
+    ec_sets = {d: {int(b) for b in synth.ec_block_indices(nb, d, w["seed"])} if d else set()
+               for d in densities}
     maxC = max(chunks)
     xs = {K: torch.randn((maxC, K), device=device, generator=gen).to(torch.float16)
           for K in {k for k, _ in shapes}}
     ys = {N: torch.empty((maxC, N), dtype=torch.float16, device=device) for N in {n for _, n in shapes}}
     # one workspace for every linear: the calls are ordered on one stream
-    b_ec = min(ec_set)
-    nws = max(spear.spear_workspace_bytes(stack[b_ec][si], maxC) for si in range(len(shapes)))
+    nws = max(spear.spear_workspace_bytes(stack[0][si], maxC) for si in range(len(shapes)))
     wbuf = torch.zeros(nws + 256, dtype=torch.uint8, device=device)
     ws = wbuf[(-wbuf.data_ptr()) % 256:][:nws]
 
-    def call(b, si, M, s):
+    def call(b, si, M, s, ec):
         K, N = shapes[si]
-        spear.spear_linear(stack[b][si], xs[K][:M], y=ys[N][:M], workspace=ws, main_stream=s)
+        lay = stack[b][si] if ec else plain[b][si]
+        spear.spear_linear(lay, xs[K][:M], y=ys[N][:M], workspace=ws, main_stream=s)
 
-    # latency table: each entry timed over the stack's blocks of that kind (cold weights)
-    kinds = {True: sorted(ec_set), False: [b for b in range(w["blocks"]) if b not in ec_set]}
+    # latency table: each entry timed over all blocks in turn (cold weights)
     lut = {}
     for si in range(len(shapes)):
-        for ec, blocks in kinds.items():
+        for ec in (True, False):
             for M in chunks + [n_dec]:
                 lut[(si, ec, M)] = graph_call_time_ms(
-                    torch, lambda i, s: call(blocks[i % len(blocks)], si, M, s), len(blocks), reps=3)
+                    torch, lambda i, s: call(i % nb, si, M, s, ec), nb, reps=3)
 
-    def predicted(C):
-        return sum(lut[(si, b in ec_set, C)] + lut[(si, b in ec_set, n_dec)]
-                   for b in range(w["blocks"]) for si in range(len(shapes)))
+    def predicted(C, ecs):
+        return sum(lut[(si, b in ecs, C)] + lut[(si, b in ecs, n_dec)]
+                   for b in range(nb) for si in range(len(shapes)))
 
-    pred = [predicted(C) for C in chunks]
-    stream = torch.cuda.Stream()
-    out = []
-    for budget in (1.0, 2.0, 4.0, 8.0, 16.0, w["budget_ms"]):
-        C, violated = spear.spear_select_chunk(chunks, pred, budget)
-
-        def step(_i, s, C=C):
-            for b in range(w["blocks"]):
+    def measured(C, ecs):
+        def step(_i, s):
+            for b in range(nb):
                 for si in range(len(shapes)):
-                    call(b, si, C, s)
-                    call(b, si, n_dec, s)
-        t = graph_call_time_ms(torch, step, 1, reps=3)
-        out.append({"budget_ms": budget, "chunk": C, "violated": bool(violated),
-                    "predicted_ms": round(pred[chunks.index(C)], 3), "measured_ms": round(t, 3),
-                    "slo_met": bool(t <= budget)})
-    ec_bytes = sum(layer_bytes(stack[b][si]) - layer_bytes(stack[b][si].without_compensator())
-                   for b in ec_set for si in range(len(shapes)))
-    all_bytes = sum(layer_bytes(l) for blk in stack for l in blk)
-    del stack, xs, ys, ws, wbuf
+                    call(b, si, C, s, b in ecs)
+                    call(b, si, n_dec, s, b in ecs)
+        return graph_call_time_ms(torch, step, 1, reps=3)
+
+    all_bytes = sum(layer_bytes(l) for blk in plain for l in blk)
+    ec_bytes_per_block = sum(layer_bytes(stack[0][si]) - layer_bytes(plain[0][si]) for si in range(len(shapes)))
+    out = {"densities": {}}
+    for d in densities:
+        ecs = ec_sets[d]
+        pred = [predicted(C, ecs) for C in chunks]
+        rec = {"ec_blocks": sorted(ecs),
+               "predicted_step_ms": dict(zip(map(str, chunks), [round(p, 3) for p in pred])),
+               "compensator_memory_pct": round(100.0 * d * ec_bytes_per_block / all_bytes, 3),
+               "budgets": []}
+        budgets = (1.0, 2.0, 4.0, 8.0, 16.0, w["budget_ms"]) if d == w["ec_blocks"] else (16.0,)
+        for budget in budgets:
+            C, violated = spear.spear_select_chunk(chunks, pred, budget)
+            t = measured(C, ecs)
+            rec["budgets"].append({"budget_ms": budget, "chunk": C, "violated": bool(violated),
+                                   "predicted_ms": round(pred[chunks.index(C)], 3),
+                                   "measured_ms": round(t, 3), "slo_met": bool(t <= budget)})
+        out["densities"][str(d)] = rec
+    del stack, plain, xs, ys, ws, wbuf
     torch.cuda.empty_cache()
-    return {"ec_blocks": sorted(ec_set), "predicted_step_ms": dict(zip(map(str, chunks), [round(p, 3) for p in pred])),
-            "compensator_memory_pct": round(100.0 * ec_bytes / (all_bytes - ec_bytes), 3),
-            "budgets": out}
+    return out
 
 
 def ceilings(torch, device):
@@ -498,6 +521,20 @@ def ceilings(torch, device):
     torch.cuda.synchronize()
     out["d2d_copy_GBps"] = round(5 * 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     del src, dst
+    # a device copy of one layer's weight bytes (4-bit words plus g128 scales and zeros), on
+    # copies rotating over >= 1 GiB as the decode bench does: the launch-to-launch floor of
+    # streaming that many bytes once (read + write counted)
+    lay_copy = {}
+    for K, N in synth.LLAMA7B_SHAPES:
+        nbytes = N * K // 2 + 4 * N * K // 128
+        n = max(2, -(-ROTATION_BYTES // nbytes))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=device) for _ in range(n)]
+        dsts = [torch.empty(nbytes, dtype=torch.uint8, device=device) for _ in range(2)]
+        t = graph_call_time_ms(torch, lambda i, st: dsts[i % 2].copy_(bufs[i]), n)
+        lay_copy[f"{K}->{N}"] = {"bytes_read": nbytes, "us": round(t * 1e3, 3),
+                                 "read_GBps": round(nbytes / (t * 1e-3) / 1e9, 1)}
+        del bufs, dsts
+    out["layer_sized_copy"] = lay_copy
     gemm = {}
     for K, N in synth.LLAMA7B_SHAPES:
         a = torch.randn((2048, K), device=device).to(torch.bfloat16)
