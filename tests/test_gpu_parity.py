@@ -336,6 +336,10 @@ PREFILL_CASES = [
     (256, 4096, 128, 32, 100, "f16", True, True),   # K split untouched by the concurrent schedule
     (192, 8192, 0, 64, 40, "f16", True, False),     # few tokens: compensator split 32 ways, summed once
     (192, 8192, 0, 64, 40, "f16", True, True),      # the same, concurrent schedule
+    # unsplit and serial: U B^T in the GEMM epilogue (bf16 hi/lo MFMAs, B prefetched)
+    (200, 512, 128, 100, 77, "f16", False, False),  # fp16 B split hi/lo; r % 8 != 0: B loaded per value; 4 rank chunks
+    (320, 768, 128, 40, 150, "f16", True, False),   # fp16, r % 8 == 0: B in 16-byte pieces, 2 chunks, ragged last
+    (256, 896, 0, 64, 129, "bf16", True, False),    # bf16 per-channel, 2 full chunks, ragged M
 ]
 
 
@@ -460,17 +464,19 @@ def test_llama7b_decode_sampled(K, N):
         assert_close(gpu_y_f64(y, "f16")[:, rows], oracle_y(hl, xb, rows=rows), f"7B {K}->{N} M={M}")
 
 
+@pytest.mark.parametrize("schedule", ["serial", "concurrent"])
 @pytest.mark.parametrize("K,N", synth.LLAMA7B_SHAPES)
-def test_llama7b_prefill_sampled(K, N):
+def test_llama7b_prefill_sampled(K, N, schedule):
     w = synth.WORKLOADS["llama7b-prefill"]
     M = w["tokens"][0]
-    note(f"llama7b prefill K={K} N={N} M={M}")
+    note(f"llama7b prefill K={K} N={N} M={M} {schedule}")
     hl = synth.make_layer(N, K, w["group_size"], w["rank"], seed=w["seed"], dtype="bf16")
     xb = synth.make_activations(M, K, seed=w["seed"], dtype="bf16", outliers=True)
     lay = spear.layer_to_device(hl, DEV)
     x = spear.act_to_device(xb, "bf16", DEV)
     ws = spear.new_workspace(lay, M)
-    y = spear.spear_linear_prefill(lay, x, workspace=ws, aux_stream=torch.cuda.Stream())
+    aux = torch.cuda.Stream() if schedule == "concurrent" else None
+    y = spear.spear_linear_prefill(lay, x, workspace=ws, aux_stream=aux)
     torch.cuda.synchronize()
     rows = sample_rows(N, 96, seed=K)
     toks = np.unique(np.r_[np.random.default_rng(N).choice(M, 48, replace=False), M - 1])
@@ -478,17 +484,19 @@ def test_llama7b_prefill_sampled(K, N):
     assert_close(gpu_y_f64(y, "bf16")[np.ix_(toks, rows)], ref, f"7B prefill {K}->{N}")
 
 
-def test_llama70b_layer_sampled():
+@pytest.mark.parametrize("schedule", ["serial", "concurrent"])
+def test_llama70b_layer_sampled(schedule):
     w = synth.WORKLOADS["llama70b-layer"]
     K, N = 8192, 28672
     hl = synth.make_layer(N, K, w["group_size"], w["rank"], seed=w["seed"], dtype="f16")
     lay = spear.layer_to_device(hl, DEV)
     rows = sample_rows(N, 96, seed=70)
     for M in w["tokens"]:
-        note(f"llama70b K={K} N={N} M={M}")
+        note(f"llama70b K={K} N={N} M={M} {schedule}")
         xb = synth.make_activations(M, K, seed=w["seed"] + M)
         x = spear.act_to_device(xb, "f16", DEV)
         ws = spear.new_workspace(lay, M)
-        y = spear.spear_linear(lay, x, workspace=ws, aux_stream=torch.cuda.Stream())
+        aux = torch.cuda.Stream() if schedule == "concurrent" else None
+        y = spear.spear_linear(lay, x, workspace=ws, aux_stream=aux)
         torch.cuda.synchronize()
         assert_close(gpu_y_f64(y, "f16")[:, rows], oracle_y(hl, xb, rows=rows), f"70B M={M}")
