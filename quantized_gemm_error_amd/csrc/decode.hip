@@ -330,12 +330,24 @@ __device__ void rank_gate_epilogue(const DecodeArgs &a, uint16_t *xs, f32x4_t (&
   const int rs = a.rank + 1, hs = a.rg_hidden + 1;
   float *tl = (float *)((char *)xs + a.rg_off);  // [16 MB][rs]
   float *hl = tl + PS * rs;                       // [16 MB][hs]
+  // each element's ks <= 16 partials are contiguous: up to four 16-byte
+  // loads, all issued before the sum, which runs in split order
+  const __amdgpu_buffer_rsrc_t pr =
+      __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
+  const int kq = a.ks / 4;
   for (int i = tid; i < a.M * a.rank; i += kThreads) {
     const int m = i / a.rank, j = i - m * a.rank;
-    const uint32_t *pp = (const uint32_t *)a.part + (size_t)(j * PS + m) * a.ks;
+    f32x4_t v[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      v[qq] = load_partials4(pr, ((j * PS + m) * a.ks + 4 * min(qq, kq - 1)) * 4);
     float t = 0.f;
-    for (int q = 0; q < a.ks; ++q)
-      t += bitcast<float>(__hip_atomic_load(pp + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      if (qq < kq) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t += v[qq][e];
+      }
     tl[m * rs + j] = t;
   }
   __syncthreads();

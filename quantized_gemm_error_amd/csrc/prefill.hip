@@ -66,6 +66,40 @@ __device__ __forceinline__ f32x4_t u_piece(const UView &u, int m, int j) {
   return in ? v : f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
+// Sums over split partials.  kSplitBatch loads (clamped to the last split, so
+// always valid) are issued before any of them is added, so a sum over ks
+// splits waits for ceil(ks / kSplitBatch) rounds of loads instead of ks; the
+// additions still run in split order.
+constexpr int kSplitBatch = 8;
+
+// sum_q p[q * stride] over q < ks, in order
+__device__ __forceinline__ float split_sum(const float *p, size_t stride, int ks) {
+  float t = 0.f;
+  for (int q0 = 0; q0 < ks; q0 += kSplitBatch) {
+    float v[kSplitBatch];
+#pragma unroll
+    for (int i = 0; i < kSplitBatch; ++i) v[i] = p[(size_t)min(q0 + i, ks - 1) * stride];
+#pragma unroll
+    for (int i = 0; i < kSplitBatch; ++i)
+      if (q0 + i < ks) t += v[i];
+  }
+  return t;
+}
+
+// the same over 16-byte pieces (p and stride 16-byte aligned)
+__device__ __forceinline__ f32x4_t split_sum4(const float *p, size_t stride, int ks) {
+  f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+  for (int q0 = 0; q0 < ks; q0 += kSplitBatch) {
+    f32x4_t v[kSplitBatch];
+#pragma unroll
+    for (int i = 0; i < kSplitBatch; ++i) v[i] = *(const f32x4_t *)(p + (size_t)min(q0 + i, ks - 1) * stride);
+#pragma unroll
+    for (int i = 0; i < kSplitBatch; ++i)
+      if (q0 + i < ks) t += v[i];
+  }
+  return t;
+}
+
 // Round to bf16 and the bf16 of the remainder: hi + lo equals v to a relative
 // 2^-16 (exactly when v has at most 16 significant bits, as fp16 values do).
 __device__ __forceinline__ void split_bf16(float v, uint16_t &hi, uint16_t &lo) {
@@ -524,8 +558,7 @@ __global__ __launch_bounds__(256) void prefill_rgate_kernel(RgArgs a) {
   for (int i = tid; i < kRgTok * a.rank; i += 256) {
     const int mm = i / a.rank, j = i - mm * a.rank;
     float t = 0.f;
-    if (m0 + mm < a.M)
-      for (int q = 0; q < a.ks; ++q) t += a.Tp[((size_t)q * a.M + m0 + mm) * a.rp1 + j];
+    if (m0 + mm < a.M) t = split_sum(a.Tp + (size_t)(m0 + mm) * a.rp1 + j, (size_t)a.M * a.rp1, a.ks);
     tl[mm][j] = t;
   }
   __syncthreads();
@@ -566,13 +599,10 @@ __global__ __launch_bounds__(256) void prefill_u_kernel(UArgs a) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= a.M * q4) return;
   const int m = i / q4, j = 4 * (i - m * q4);
-  f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-  float z = 0.f;
-  for (int q = 0; q < a.ks; ++q) {
-    const float *row = a.Tp + ((size_t)q * a.M + m) * a.rp1;
-    t += *(const f32x4_t *)(row + j);
-    z += row[a.rank];
-  }
+  const float *row = a.Tp + (size_t)m * a.rp1;
+  const size_t stride = (size_t)a.M * a.rp1;
+  const f32x4_t t = split_sum4(row + j, stride, a.ks);
+  const float z = split_sum(row + a.rank, stride, a.ks);
   const float g = gate_sigmoid(z + a.b_gate);
   f32x4_t u;
 #pragma unroll
@@ -625,15 +655,14 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(FinishArgs a) {
     if (m < a.M) {
       if constexpr (PARTS) {
         const bool vec = (a.N % 4) == 0 && n + 4 <= a.N;
-        for (int q = 0; q < a.ks; ++q) {
-          const float *src = a.part + ((size_t)q * a.M + m) * a.N + n;
-          if (vec) {
-            v += *(const f32x4_t *)src;
-          } else {
+        const float *src = a.part + (size_t)m * a.N + n;
+        const size_t stride = (size_t)a.M * a.N;
+        if (vec) {
+          v = split_sum4(src, stride, a.ks);
+        } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-              if (n + c < a.N) v[c] += src[c];
-          }
+          for (int c = 0; c < 4; ++c)
+            if (n + c < a.N) v[c] = split_sum(src + c, stride, a.ks);
         }
         if constexpr (PERCH) {
 #pragma unroll
