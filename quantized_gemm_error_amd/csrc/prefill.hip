@@ -55,17 +55,6 @@ struct UView {
   int M, rank, rp1;
 };
 
-// Four consecutive columns j..j+3 of row m, zeros for rows past M or columns
-// past the row.  The load itself is always made (from a clamped, valid
-// address) and the zeros selected afterwards, so that a batch of these loads
-// has no branches and stays in flight together.
-__device__ __forceinline__ f32x4_t u_piece(const UView &u, int m, int j) {
-  const bool in = m < u.M && j < u.rp1;
-  const f32x4_t v =
-      *(const f32x4_t *)(u.U + (size_t)min(m, u.M - 1) * u.rp1 + min(j, u.rp1 - 4));
-  return in ? v : f32x4_t{0.f, 0.f, 0.f, 0.f};
-}
-
 // Sums over split partials.  kSplitBatch loads (clamped to the last split, so
 // always valid) are issued before any of them is added, so a sum over ks
 // splits waits for ceil(ks / kSplitBatch) rounds of loads instead of ks; the
@@ -73,28 +62,30 @@ __device__ __forceinline__ f32x4_t u_piece(const UView &u, int m, int j) {
 constexpr int kSplitBatch = 8;
 
 // sum_q p[q * stride] over q < ks, in order
+template <int NB = kSplitBatch>
 __device__ __forceinline__ float split_sum(const float *p, size_t stride, int ks) {
   float t = 0.f;
-  for (int q0 = 0; q0 < ks; q0 += kSplitBatch) {
-    float v[kSplitBatch];
+  for (int q0 = 0; q0 < ks; q0 += NB) {
+    float v[NB];
 #pragma unroll
-    for (int i = 0; i < kSplitBatch; ++i) v[i] = p[(size_t)min(q0 + i, ks - 1) * stride];
+    for (int i = 0; i < NB; ++i) v[i] = p[(size_t)min(q0 + i, ks - 1) * stride];
 #pragma unroll
-    for (int i = 0; i < kSplitBatch; ++i)
+    for (int i = 0; i < NB; ++i)
       if (q0 + i < ks) t += v[i];
   }
   return t;
 }
 
 // the same over 16-byte pieces (p and stride 16-byte aligned)
+template <int NB = kSplitBatch>
 __device__ __forceinline__ f32x4_t split_sum4(const float *p, size_t stride, int ks) {
   f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-  for (int q0 = 0; q0 < ks; q0 += kSplitBatch) {
-    f32x4_t v[kSplitBatch];
+  for (int q0 = 0; q0 < ks; q0 += NB) {
+    f32x4_t v[NB];
 #pragma unroll
-    for (int i = 0; i < kSplitBatch; ++i) v[i] = *(const f32x4_t *)(p + (size_t)min(q0 + i, ks - 1) * stride);
+    for (int i = 0; i < NB; ++i) v[i] = *(const f32x4_t *)(p + (size_t)min(q0 + i, ks - 1) * stride);
 #pragma unroll
-    for (int i = 0; i < kSplitBatch; ++i)
+    for (int i = 0; i < NB; ++i)
       if (q0 + i < ks) t += v[i];
   }
   return t;
@@ -601,8 +592,9 @@ __global__ __launch_bounds__(256) void prefill_u_kernel(UArgs a) {
   const int m = i / q4, j = 4 * (i - m * q4);
   const float *row = a.Tp + (size_t)m * a.rp1;
   const size_t stride = (size_t)a.M * a.rp1;
-  const f32x4_t t = split_sum4(row + j, stride, a.ks);
-  const float z = split_sum(row + a.rank, stride, a.ks);
+  // up to 64 splits: 16 loads of each kind in flight per round
+  const f32x4_t t = split_sum4<16>(row + j, stride, a.ks);
+  const float z = split_sum<16>(row + a.rank, stride, a.ks);
   const float g = gate_sigmoid(z + a.b_gate);
   f32x4_t u;
 #pragma unroll
@@ -645,6 +637,31 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(FinishArgs a) {
   const int col = lane & 15, h = lane >> 4;
   const int n0 = blockIdx.x * kFT, m0 = blockIdx.y * kFT;
 
+  // EC: this thread's share of a rank chunk, 2 pieces of U (4 ranks of a
+  // row) and 8 values of B, read raw from clamped, valid addresses and masked
+  // when staged.  Chunk 0 is loaded first, so that its loads are in flight
+  // with the base tile's.
+  f32x4_t u_pre[2];
+  uint16_t b_pre[8];
+  auto ec_load = [&](int j0) {
+    const UView &e = a.u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = tid + 256 * i;  // 64 rows x 8 pieces
+      const int r = p >> 3, j = j0 + 4 * (p & 7);
+      u_pre[i] = *(const f32x4_t *)(e.U + (size_t)min(m0 + r, a.M - 1) * e.rp1 + min(j, e.rp1 - 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = tid + 256 * i;  // 64 rows x 32 ranks
+      const int r = p >> 5, j = j0 + (p & 31);
+      b_pre[i] = a.B[(size_t)min(n0 + r, a.N - 1) * e.rank + min(j, e.rank - 1)];
+    }
+  };
+  if constexpr (EC) {
+    if (a.u.rank > 0) ec_load(0);
+  }
+
   // --- base tile: 64 rows x 16 pieces of 4
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -681,19 +698,20 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(FinishArgs a) {
   if constexpr (EC) {
     const UView &e = a.u;
     for (int j0 = 0; j0 < e.rank; j0 += kFRc) {
+      if (j0 > 0) ec_load(j0);
       __syncthreads();  // base tile written; the previous chunk's readers are done
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int p = tid + 256 * i;  // 64 rows x 8 pieces
         const int r = p >> 3, q = p & 7;
-        *(f32x4_t *)&us[r][4 * q] = u_piece(e, m0 + r, j0 + 4 * q);
+        const bool in = m0 + r < a.M && j0 + 4 * q < e.rp1;
+        *(f32x4_t *)&us[r][4 * q] = in ? u_pre[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int p = tid + 256 * i;  // 64 rows x 32 ranks
         const int r = p >> 5, jj = p & 31;
-        bs[r][jj] = (n0 + r < a.N && j0 + jj < e.rank)
-                        ? to_f32<DT>(a.B[(size_t)(n0 + r) * e.rank + j0 + jj]) : 0.f;
+        bs[r][jj] = (n0 + r < a.N && j0 + jj < e.rank) ? to_f32<DT>(b_pre[i]) : 0.f;
       }
       __syncthreads();
       const int tk = 16 * wave + col;  // A-operand row (token) of this lane
