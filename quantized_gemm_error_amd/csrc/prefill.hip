@@ -686,6 +686,10 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(FinishArgs a) {
           for (int c = 0; c < 4; ++c)
             v[c] *= (n + c < a.N) ? (float)bitcast<_Float16>(a.scales[n + c]) : 0.f;
         }
+      } else if ((a.N % 4) == 0 && n + 4 <= a.N && ((uintptr_t)a.y % 8) == 0) {
+        const uint2 w = *(const uint2 *)(a.y + (size_t)m * a.N + n);  // 4 values in one load
+        v = f32x4_t{to_f32<DT>((uint16_t)w.x), to_f32<DT>((uint16_t)(w.x >> 16)),
+                    to_f32<DT>((uint16_t)w.y), to_f32<DT>((uint16_t)(w.y >> 16))};
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
