@@ -243,11 +243,12 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
 
   // EPI operands of one rank chunk: this thread's 4 pieces of U (4 ranks of
   // a row each) and, when r % 8 == 0 and B is 16-byte aligned, its 2 pieces of
-  // B (8 ranks of a row each).  epi_load reads them raw from clamped, valid
-  // addresses; epi_value selects zeros for rows past M or N and ranks past r
-  // when they are staged.  The first chunk is loaded during the last k-block,
-  // and as nothing reads the registers before the staging, the loads stay in
-  // flight behind that block's MFMAs.
+  // B (8 ranks of a row each; otherwise B is read value by value when the
+  // chunk is staged).  epi_load reads them raw from clamped, valid addresses;
+  // the staging selects zeros for rows past M or N and ranks past r.  The
+  // first chunk is loaded during the last k-block, and as nothing reads the
+  // registers before the staging, the loads stay in flight behind that
+  // block's MFMAs.
   f32x4_t u_pre[4];
   u16x8_t b_pre[2];
   const bool bvec = (a.u.rank % 8) == 0 && ((uintptr_t)a.B % 16) == 0;
