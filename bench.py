@@ -447,7 +447,7 @@ def serving_context(torch, device):
     densities = (0, w["ec_blocks"], 8, 16, nb)
     ec_sets = {d: {int(b) for b in synth.ec_block_indices(nb, d, w["seed"])} if d else set()
                for d in densities}
-    maxC = max(chunks)
+    maxC = max(chunks) + n_dec
     xs = {K: torch.randn((maxC, K), device=device, generator=gen).to(torch.float16)
           for K in {k for k, _ in shapes}}
     ys = {N: torch.empty((maxC, N), dtype=torch.float16, device=device) for N in {n for _, n in shapes}}
@@ -473,12 +473,15 @@ def serving_context(torch, device):
         return sum(lut[(si, b in ecs, C)] + lut[(si, b in ecs, n_dec)]
                    for b in range(nb) for si in range(len(shapes)))
 
-    def measured(C, ecs):
+    def measured(C, ecs, merged=False):
         def step(_i, s):
             for b in range(nb):
                 for si in range(len(shapes)):
-                    call(b, si, C, s, b in ecs)
-                    call(b, si, n_dec, s, b in ecs)
+                    if merged:   # the chunk and the decode tokens as one batch of C + n_dec rows
+                        call(b, si, C + n_dec, s, b in ecs)
+                    else:
+                        call(b, si, C, s, b in ecs)
+                        call(b, si, n_dec, s, b in ecs)
         return graph_call_time_ms(torch, step, 1, reps=3)
 
     all_bytes = sum(layer_bytes(l) for blk in plain for l in blk)
@@ -498,6 +501,12 @@ def serving_context(torch, device):
             rec["budgets"].append({"budget_ms": budget, "chunk": C, "violated": bool(violated),
                                    "predicted_ms": round(pred[chunks.index(C)], 3),
                                    "measured_ms": round(t, 3), "slo_met": bool(t <= budget)})
+        if d == w["ec_blocks"]:
+            # merged mixed batch: each linear runs once on the chunk's C rows plus the decode
+            # tokens' rows (the prefill path), against the two separate calls
+            rec["merged_vs_separate_ms"] = {str(C): {"separate": round(measured(C, ecs), 3),
+                                                     "merged": round(measured(C, ecs, merged=True), 3)}
+                                            for C in chunks}
         out["densities"][str(d)] = rec
     del stack, plain, xs, ys, ws, wbuf
     torch.cuda.empty_cache()
