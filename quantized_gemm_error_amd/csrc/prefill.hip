@@ -813,6 +813,26 @@ static int gemm_ksplit(int M, int N, int K) {
   return (nkb + per - 1) / per;  // no empty split
 }
 
+// Rows of a ragged tail.  An unsplit GEMM whose tiles are a few more than a
+// whole number of workgroups per CU (256 CUs) leaves the CUs that get one
+// more tile working while the rest wait: with 288 tiles, 32 CUs hold two
+// workgroups and take up to twice as long.  Its last tile rows then go to a
+// K-split GEMM of their own, whose workgroups are short, and to the finish
+// kernel.  Returns how many rows that is (0: none): the rows past the whole
+// tile rows that fit the whole number of workgroups per CU, when their tiles
+// are at most a quarter of the CUs and can be split.
+constexpr int kGemmCus = 256;
+static int prefill_tail_rows(int M, int N, int K) {
+  const int ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM;
+  const int T = ntn * ntm;
+  if (T <= kGemmCus || gemm_ksplit(M, N, K) > 1) return 0;
+  const int main_tile_rows = (T / kGemmCus) * kGemmCus / ntn;
+  const int tail_tiles = T - main_tile_rows * ntn;
+  if (main_tile_rows == 0 || tail_tiles == 0 || tail_tiles * 4 > kGemmCus) return 0;
+  const int tail = M - main_tile_rows * BM;
+  return gemm_ksplit(tail, N, K) > 1 ? tail : 0;
+}
+
 // Workspace layout after the 2048-byte header: the compensator's split
 // partials [ks][M][rp1], U [M][rp1] formed from them, and the GEMM's
 // split partials (at most kGemmSplitWgs tiles of 128 x 128 fp32).  All are
@@ -928,7 +948,44 @@ hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint
 
   if (!concurrent) {
     if (ec && (e = launch_ec(main_s)) != hipSuccess) return e;
-    return launch_main(ec);
+    const int tail = ws ? prefill_tail_rows(M, L.N, L.K) : 0;
+    if (tail == 0) return launch_main(ec);
+    // rows [0, Mm): the unsplit GEMM (with U B^T in its epilogue when
+    // compensated); rows [Mm, M): a K-split GEMM and the finish kernel
+    const int Mm = M - tail;
+    GemmArgs gm = g;
+    gm.M = Mm;
+    if (dtype == DT_F16)
+      L.per_channel ? launch_gemm<DT_F16, true>(gm, dim3(ggrid.x, Mm / BM, 1), ec, main_s)
+                    : launch_gemm<DT_F16, false>(gm, dim3(ggrid.x, Mm / BM, 1), ec, main_s);
+    else
+      L.per_channel ? launch_gemm<DT_BF16, true>(gm, dim3(ggrid.x, Mm / BM, 1), ec, main_s)
+                    : launch_gemm<DT_BF16, false>(gm, dim3(ggrid.x, Mm / BM, 1), ec, main_s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int tks = gemm_ksplit(tail, L.N, L.K);
+    const UView ut = ec ? UView{uv.U + (size_t)Mm * uv.rp1, tail, uv.rank, uv.rp1} : UView{};
+    GemmArgs gt = g;
+    gt.x = x + (size_t)Mm * L.K;
+    gt.y = y + (size_t)Mm * L.N;
+    gt.M = tail;
+    gt.u = ut;
+    gt.ks = tks;
+    gt.part = (float *)(base + w.gpart);
+    const dim3 tgrid(ggrid.x, (tail + BM - 1) / BM, tks);
+    if (dtype == DT_F16)
+      L.per_channel ? launch_gemm<DT_F16, true>(gt, tgrid, false, main_s)
+                    : launch_gemm<DT_F16, false>(gt, tgrid, false, main_s);
+    else
+      L.per_channel ? launch_gemm<DT_BF16, true>(gt, tgrid, false, main_s)
+                    : launch_gemm<DT_BF16, false>(gt, tgrid, false, main_s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const FinishArgs ft{gt.y, gt.part, tks, L.scales, ut, L.B, L.N, tail};
+    const dim3 tfgrid((L.N + kFT - 1) / kFT, (tail + kFT - 1) / kFT);
+    if (dtype == DT_F16)
+      launch_finish<DT_F16, true>(ft, tfgrid, L.per_channel, ec, main_s);
+    else
+      launch_finish<DT_BF16, true>(ft, tfgrid, L.per_channel, ec, main_s);
+    return hipGetLastError();
   }
 
   // concurrent: compensator on aux alongside the GEMM; U B^T after the join

@@ -355,6 +355,30 @@ def test_prefill_parity(N, K, G, r, M, dtype, outl, aux):
     assert_close(gpu_y_f64(y, dtype), oracle_y(hl, xb), f"prefill {N}x{K} M={M}")
 
 
+# Tiles just past a whole number of workgroups per CU (2080 rows x 32 column
+# tiles = 544 = 2 x 256 + 32; 1056 rows: 288 = 256 + 32): the last rows run as
+# a K-split GEMM plus the finish kernel.
+TAIL_CASES = [
+    # N, K, G, r, M, dtype
+    (4096, 1024, 128, 32, 2080, "f16"),
+    (4096, 1024, 128, 32, 1056, "bf16"),
+    (4096, 1024, 1024, 24, 2090, "bf16"),  # per-channel, 42 tail rows
+    (4096, 1024, 128, 0, 2080, "bf16"),    # rank 0 with a workspace
+]
+
+
+@pytest.mark.parametrize("N,K,G,r,M,dtype", TAIL_CASES)
+def test_prefill_ragged_tail(N, K, G, r, M, dtype):
+    note(f"prefill tail N={N} K={K} G={G} r={r} M={M} {dtype}")
+    hl, xb, lay, x = _setup(N, K, G, r, seed=N + K + M + r, dtype=dtype, M=M, outliers=True,
+                            b_gate=0.2)
+    ws = spear.new_workspace(lay, M)
+    y = spear.spear_linear_prefill(lay, x, workspace=ws)
+    torch.cuda.synchronize()
+    rows = sample_rows(N, 160, seed=M)
+    assert_close(gpu_y_f64(y, dtype)[:, rows], oracle_y(hl, xb, rows=rows), f"tail {M} rows")
+
+
 def test_prefill_gate_off_matches_rank_zero():
     note("prefill gate off")
     hl, xb, lay, x = _setup(256, 512, 128, 32, seed=11, M=96)
