@@ -427,6 +427,9 @@ def rank_gate_context(torch, device):
     return out
 
 
+PROMPT = 8192  # prompt length for the serving leg's time-to-first-token figures
+
+
 def serving_context(torch, device):
     """Chunked serving over a 32-block stack of the three 7B projections (random-init g128
     4-bit; every block carries a rank-32 compensator, and a density d switches on those of d
@@ -494,6 +497,12 @@ def serving_context(torch, device):
                "predicted_step_ms": dict(zip(map(str, chunks), [round(p, 3) for p in pred])),
                "compensator_memory_pct": round(100.0 * d * ec_bytes_per_block / all_bytes, 3),
                "budgets": []}
+        # a prompt of PROMPT tokens prefilled in chunks of C while 32 decode tokens run along:
+        # time to first token = ceil(PROMPT / C) steps; inter-token latency of the decode
+        # tokens meanwhile = one step (both predicted from the table)
+        rec["prompt_tokens"] = PROMPT
+        rec["ttft_itl_ms"] = {str(C): {"ttft": round(-(-PROMPT // C) * p, 3), "itl": round(p, 3)}
+                              for C, p in zip(chunks, pred)}
         budgets = (1.0, 2.0, 4.0, 8.0, 16.0, w["budget_ms"]) if d == w["ec_blocks"] else (16.0,)
         for budget in budgets:
             C, violated = spear.spear_select_chunk(chunks, pred, budget)
