@@ -114,7 +114,8 @@ class DecodeWorkload:
                 self.x[(K, M)] = xt[:M].contiguous()
         self.y = {(N, M): torch.empty((M, N), dtype=torch.float16, device=device)
                   for _, N in self.shapes for M in self.tokens}
-        self.ws = [spear.new_workspace(l, maxM) for l in base] if self.r > 0 else None
+        # rank 0 gets a workspace too, so that it takes the same (split-K) launch shapes
+        self.ws = [spear.new_workspace(l, maxM) for l in base]
         # the calls of one step: (shape index, M)
         self.calls = [(si, M) for M in self.tokens for si in range(len(self.shapes))]
         self.step_bytes = sum(call_bytes(self.shapes[si][1], self.shapes[si][0], self.G, self.r, M)
@@ -636,12 +637,13 @@ def dominant_sources_sha256():
 
 
 def _decode_template_args(name):
-    """(DT, MB, EC, PERCH, XMODE, WR) of a decode_kernel instantiation, else None."""
-    key = "decode_kernel<"
-    if key not in name:
-        return None
-    inner = name[name.index(key) + len(key):].split(">")[0]
-    return tuple(t.strip() for t in inner.split(","))
+    """(DT, MB, EC, PERCH, ...) of a decode_kernel or decode_split_kernel instantiation, else
+    None."""
+    for key in ("decode_kernel<", "decode_split_kernel<"):
+        if key in name:
+            inner = name[name.index(key) + len(key):].split(">")[0]
+            return tuple(t.strip() for t in inner.split(","))
+    return None
 
 
 def _is_dominant(name):
@@ -716,9 +718,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
                       f"per launch; trace span / bench = {span_us / b_us:.3f}."]
     lines = ["# decode_kernel, Llama-7B decode projections: rocprofv3 kernel trace", "",
              "Command (repository root, one MI355X):", "", "    " + TRACE_CMD, "",
-             "Dominant kernel: decode_kernel with one 16-token block (M <= 16) and the "
-             "compensator, all its instantiations (the three shapes select the row-block "
-             "width and the staging mode).", "",
+             "Dominant kernel: the decode kernels with one 16-token block (M <= 16) and the "
+             "compensator, all their instantiations (the three shapes and M select the "
+             "row-block width, the staging mode and, for the 11008-wide K at M = 16, the "
+             "split-K launch decode_split_kernel).", "",
              f"- dispatches: {len(dom)}",
              f"- mean kernel duration: {statistics.mean(dur):.3f} us (median {statistics.median(dur):.3f})",
              f"- mean start-to-start spacing of consecutive dispatches: "
@@ -775,7 +778,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
                      f"{(fm / f_scale + wm / w_scale) * 1024 / 1e6:.3f} |")
     with open(os.path.join(out_dir, "decode_kernel_llama7b_hbm_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    rec = {"kernel": "decode_kernel, M <= 16, compensated (all instantiations)",
+    rec = {"kernel": "decode_kernel and decode_split_kernel, M <= 16, compensated (all instantiations)",
            "kernel_sources_sha256": dominant_sources_sha256(),
            "traffic_bytes_per_launch": int(round(traffic)),
            "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b)),
@@ -949,7 +952,7 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                 "traffic_note": traffic_note,
-                "kernel": "decode_kernel<f16, one 16-token block, compensated, group-wise>",
+                "kernel": "decode_kernel / decode_split_kernel<f16, one 16-token block, compensated, group-wise>",
                 "avg_launch_us": round(dom_ms / n_launch * 1e3, 3), "launches_timed": n_launch,
                 "bytes_per_launch_avg": int(dom_bytes / len(dom_calls))}
     two_calls = [wl.calls[c] for c in classes["two_blocks"]]

@@ -134,8 +134,11 @@ size_t spear_workspace_bytes(const spear_layer_t *layer, int32_t M) {
   if (check_layer(layer, &d) != SPEAR_OK || M < 0) return 0;
   // enough for every call with 1..M tokens: both needs grow with M
   size_t need = prefill_workspace_bytes(d, M < 1 ? 1 : M);
-  const size_t dec = decode_workspace_bytes(d, M < 1 ? 1 : (M < SPEAR_MAX_DECODE_M ? M : SPEAR_MAX_DECODE_M));
-  if (dec > need) need = dec;
+  const int dm = M < 1 ? 1 : (M < SPEAR_MAX_DECODE_M ? M : SPEAR_MAX_DECODE_M);
+  for (int m = 1; m <= dm; ++m) {  // the split launch's needs vary with M's tile plan
+    const size_t dec = decode_fast_workspace_bytes(d, m);
+    if (dec > need) need = dec;
+  }
   return need < 256 ? 256 : need;
 }
 
@@ -164,6 +167,7 @@ spear_status_t spear_linear_decode(const spear_layer_t *layer, spear_dtype_t dty
   if ((st = check_ws(workspace, workspace_bytes, decode_workspace_bytes(d, M))) != SPEAR_OK)
     return st;
   return hip_status(launch_decode(d, (int)dtype, (const uint16_t *)x, (uint16_t *)y, M, workspace,
+                                  aligned(workspace, 256) ? workspace_bytes : 0,
                                   (hipStream_t)stream),
                     "decode launch");
 }
@@ -204,6 +208,24 @@ spear_status_t spear_set_decode_max_m(int32_t m) {
 }
 
 int32_t spear_get_decode_max_m(void) { return g_decode_max_m.load(); }
+
+spear_status_t spear_set_decode_split_min_m(int32_t m) {
+  if (m < 1 || m > SPEAR_MAX_DECODE_M + 1)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode_split_min_m=%d outside 1..%d", m,
+                SPEAR_MAX_DECODE_M + 1);
+  set_decode_split_min_m(m);
+  return ok();
+}
+
+int32_t spear_get_decode_split_min_m(void) { return get_decode_split_min_m(); }
+
+spear_status_t spear_set_decode_split_min_k(int32_t k) {
+  if (k < 1) return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode_split_min_k=%d must be >= 1", k);
+  set_decode_split_min_k(k);
+  return ok();
+}
+
+int32_t spear_get_decode_split_min_k(void) { return get_decode_split_min_k(); }
 
 int32_t spear_select_chunk(const int32_t *chunks, const float *pred_ms, int32_t n, float budget_ms,
                            int32_t *violated) {

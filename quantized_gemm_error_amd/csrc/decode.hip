@@ -24,19 +24,29 @@
 // side, 16-byte buffer loads with the sc1 cache policy (the same access that
 // a relaxed agent-scope atomic load makes), which are coherent across the
 // XCDs' separate L2 caches on their own, so no wave needs a cache-wide
-// invalidate; only the producers' release (before they count themselves in)
-// writes back their L2.  The K-splits of one element sit next to each other,
-// so a consumer gathers them with ks / 4 loads, all in flight at once.
+// invalidate or write-back: a producer only waits for its stores to complete
+// before it counts itself in.  The K-splits of one element sit next to each
+// other, so a consumer gathers them with ks / 4 loads, all in flight at once.
+// Those uncached loads cost far more per CU than cached ones, so no gather
+// issues a load it does not need.
+//
+// With more tokens and a long K, every consumer staging all of x dominates
+// (workgroups x M K 2 bytes from L2).  From a token threshold on, the launch
+// instead splits K across the workgroups of each 128-row output tile
+// (consume_split): x is staged once per tile and K-split, and the split that
+// completes a tile sums the tile's partials and adds the compensator.
 //
 // Every loop that touches memory has a compile-time shape, so its loads
 // issue back to back and the waits count them exactly.  The last workgroup
 // to finish (counted over eight slots, then across the slots) resets the
 // workspace counters for the next call.
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
+
 
 namespace spear {
 
@@ -79,6 +89,11 @@ struct DecodeArgs {
   int red_off;     // byte offset of the wave-reduction buffer in dynamic LDS
   WsHeader *hdr;
   float *part;     // [rb_a][16 rows of A'][16 * MB tokens][ks]: a split's sums are contiguous
+  // split-K consumers
+  int ksp, nbs;    // K-splits per 128-row tile; 128-wide blocks per split
+  int ngs;         // scale/zero table groups per row
+  int party_bytes;
+  float *party;    // partial output tiles (split_piece_off)
 };
 
 // Sum of the waves' partial tiles in a fixed order (wave 0's own, then 1..7).
@@ -95,6 +110,18 @@ __device__ __forceinline__ f32x4_t reduce_waves(f32x4_t own, f32x4_t (*red)[MB][
 // (cache policy sc1, as a relaxed agent-scope atomic load has).
 __device__ __forceinline__ f32x4_t load_partials4(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return bitcast<f32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16));
+}
+
+// Completion of this wave's agent-scope stores before the count that
+// publishes them.  Those stores (sc1) are written through to the level that
+// every XCD reads with sc1 loads, so they need no write-back of the L2, only
+// an s_waitcnt vmcnt(0) (gfx9 counts stores in vmcnt; this encoding leaves
+// expcnt and lgkmcnt at their maxima).  The signal fences keep the compiler
+// from moving memory operations across the wait.
+__device__ __forceinline__ void publish_wait() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // ---------------------------------------------------------------------------
@@ -159,7 +186,7 @@ __device__ void produce(const DecodeArgs &a, int p, f32x4_t (*red)[MB][64], int 
         __hip_atomic_store(&dst[(size_t)(16 * mb + 4 * h + e) * a.ks], bitcast<uint32_t>(v[e]),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    publish_wait();
     if (lane == 0)
       __hip_atomic_fetch_add(&a.hdr->arrive.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -378,6 +405,86 @@ __device__ void rank_gate_epilogue(const DecodeArgs &a, uint16_t *xs, f32x4_t (&
   }
 }
 
+// The compensator in a consumer's epilogue, after its main loop: wait for
+// the producers, then add u B^T for the wave's rows, u = g * (A x) with the
+// scalar gate (or the per-rank gate's u).  Each of a row-block's KG waves
+// takes every KG-th rank step, starting at wk.
+template <int DT, int MB, int KG>
+__device__ void ec_epilogue(const DecodeArgs &a, uint16_t *xs, f32x4_t (&acc)[MB], int row, int wk,
+                            int tid) {
+  const int lane = tid & 63, col = lane & 15, h = lane >> 4;
+  // element (j, m) of [A; w_g] x is the sum of its ks partials at
+  // ((j * 16 MB + m) * ks + [0, ks)) in the partial array
+  const int PS = 16 * MB;
+  const int nst = (a.rank + 3) / 4;  // rank steps of four; this wave takes st = wk + KG i
+  // B for the wave's first rank step does not depend on the producers
+  float b_first = 0.f;
+  if (wk < nst) b_first = to_f32<DT>(a.B[(size_t)row * a.rank + min(4 * wk + h, a.rank - 1)]);
+  wait_producers(a, tid);
+  if (a.rg_hidden > 0) {
+    rank_gate_epilogue<DT, MB, KG>(a, xs, acc, row, wk, tid);
+  } else {
+  const __amdgpu_buffer_rsrc_t pr =
+      __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
+  const int kq = a.ks / 4;
+  float g[MB];
+  // one rank step; the first also gathers the gate row j = rank, with its
+  // loads in flight together with the step's own
+  auto step = [&](int st, float bval, auto gate_tag) {
+    constexpr bool kGate = decltype(gate_tag)::value;
+    const int j = min(4 * st + h, a.rank - 1);
+    float t[MB], z[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) t[mb] = z[mb] = 0.f;
+    for (int q0 = 0; q0 < kq; q0 += 2) {
+      f32x4_t tv[MB][2], zv[MB][2];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          // uncached loads are costly per CU: none past the element's ks partials, and
+          // the gate row only in the h == 0 lanes (shared with the others below)
+          const int q = q0 + qq;
+          tv[mb][qq] = zv[mb][qq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (q < kq) {
+            tv[mb][qq] = load_partials4(pr, (((j * PS + col + 16 * mb) * a.ks) + 4 * q) * 4);
+            if (kGate && h == 0)
+              zv[mb][qq] = load_partials4(pr, (((a.rank * PS + col + 16 * mb) * a.ks) + 4 * q) * 4);
+          }
+        }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          if (q0 + qq < kq) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              t[mb] += tv[mb][qq][e];
+              if constexpr (kGate) z[mb] += zv[mb][qq][e];
+            }
+          }
+        }
+    }
+    if constexpr (kGate) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) g[mb] = gate_sigmoid(__shfl(z[mb], col) + a.b_gate);
+    }
+    const bool jin = 4 * st + h < a.rank;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const float u = (jin && col + 16 * mb < a.M) ? g[mb] * t[mb] : 0.f;
+      acc[mb] = mfma_16x16x4_f32(u, jin ? bval : 0.f, acc[mb]);
+    }
+  };
+  if (wk < nst) {
+    step(wk, b_first, std::true_type{});
+    for (int st = wk + KG; st < nst; st += KG)
+      step(st, to_f32<DT>(a.B[(size_t)row * a.rank + min(4 * st + h, a.rank - 1)]),
+           std::false_type{});
+  }
+  }  // scalar gate
+}
+
 // ---------------------------------------------------------------------------
 // Consumers: 16 * WR output rows, full K.  The eight waves form WR row-blocks
 // of KG = 8 / WR waves; the KG waves of a row-block take interleaved K blocks
@@ -529,73 +636,7 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
     for (int mb = 0; mb < MB; ++mb) acc[mb] *= s_row;
   }
 
-  if constexpr (EC) {
-    // element (j, m) of [A; w_g] x is the sum of its ks partials at
-    // ((j * 16 MB + m) * ks + [0, ks)) in the partial array
-    const int PS = 16 * MB;
-    const int nst = (a.rank + 3) / 4;  // rank steps of four; this wave takes st = wk + KG i
-    // B for the wave's first rank step does not depend on the producers
-    float b_first = 0.f;
-    if (wk < nst) b_first = to_f32<DT>(a.B[(size_t)row * a.rank + min(4 * wk + h, a.rank - 1)]);
-    wait_producers(a, tid);
-    if (a.rg_hidden > 0) {
-      rank_gate_epilogue<DT, MB, KG>(a, xs, acc, row, wk, tid);
-    } else {
-    const __amdgpu_buffer_rsrc_t pr =
-        __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
-    const int kq = a.ks / 4;
-    float g[MB];
-    // one rank step; the first also gathers the gate row j = rank, with its
-    // loads in flight together with the step's own
-    auto step = [&](int st, float bval, auto gate_tag) {
-      constexpr bool kGate = decltype(gate_tag)::value;
-      const int j = min(4 * st + h, a.rank - 1);
-      float t[MB], z[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) t[mb] = z[mb] = 0.f;
-      for (int q0 = 0; q0 < kq; q0 += 2) {
-        f32x4_t tv[MB][2], zv[MB][2];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int qq = 0; qq < 2; ++qq) {
-            const int q = min(q0 + qq, kq - 1);
-            tv[mb][qq] = load_partials4(pr, (((j * PS + col + 16 * mb) * a.ks) + 4 * q) * 4);
-            if constexpr (kGate)
-              zv[mb][qq] = load_partials4(pr, (((a.rank * PS + col + 16 * mb) * a.ks) + 4 * q) * 4);
-          }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int qq = 0; qq < 2; ++qq) {
-            if (q0 + qq < kq) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                t[mb] += tv[mb][qq][e];
-                if constexpr (kGate) z[mb] += zv[mb][qq][e];
-              }
-            }
-          }
-      }
-      if constexpr (kGate) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) g[mb] = gate_sigmoid(z[mb] + a.b_gate);
-      }
-      const bool jin = 4 * st + h < a.rank;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const float u = (jin && col + 16 * mb < a.M) ? g[mb] * t[mb] : 0.f;
-        acc[mb] = mfma_16x16x4_f32(u, jin ? bval : 0.f, acc[mb]);
-      }
-    };
-    if (wk < nst) {
-      step(wk, b_first, std::true_type{});
-      for (int st = wk + KG; st < nst; st += KG)
-        step(st, to_f32<DT>(a.B[(size_t)row * a.rank + min(4 * st + h, a.rank - 1)]),
-             std::false_type{});
-    }
-    }  // scalar gate
-  }
+  if constexpr (EC) ec_epilogue<DT, MB, KG>(a, xs, acc, row, wk, tid);
 
   // fixed-order sum over the row-block's KG waves
   if (wk > 0) {
@@ -616,6 +657,328 @@ __device__ void consume(const DecodeArgs &a, int tile, uint16_t *xs, f32x4_t (*r
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K consumers (ksp > 1).  Consumer c takes output tile c / ksp (128
+// rows: one 16-row block per wave) and K-split c % ksp (nbs consecutive
+// 128-wide blocks).  x is staged once per workgroup for its split only, so a
+// call stages M K 2 bytes per tile instead of per 16 rows.  Each wave runs its
+// rows over the split and stores its fp32 partial tile; the workgroup that
+// completes a tile (its arrival counter reaches ksp) sums the tile's ksp
+// partials in split order, adds the compensator and rounds y once.
+// ---------------------------------------------------------------------------
+
+// Byte offset of wave w's partial for 16-token block mb, split q, tile t:
+// [ksp][tiles][8 waves][MB][64 lanes] 16-byte pieces.
+template <int MB>
+__device__ __forceinline__ int split_piece_off(const DecodeArgs &a, int q, int t, int w, int mb,
+                                               int lane) {
+  return ((((q * a.n_tiles + t) * kWaves + w) * MB + mb) * 64 + lane) * 16;
+}
+
+// The compensator of a completed tile: the workgroup gathers [A; w_g] x for
+// every token into LDS (each element the sum of its ks producer partials in
+// split order), forms u (the scalar gate's g t, or the per-rank gate's
+// alpha gamma(t) t) and each wave adds u B^T for its 16 rows.
+template <int DT, int MB>
+__device__ void split_ec_epilogue(const DecodeArgs &a, uint16_t *xs, f32x4_t (&acc)[MB], int row,
+                                  int tid) {
+  const int lane = tid & 63, col = lane & 15, h = lane >> 4;
+  const int PS = 16 * MB;
+  const int rows = a.rows;             // rank (+ the gate row with the scalar gate)
+  const int rs = a.rank + 1, hs = a.rg_hidden + 1;
+  float *tl = (float *)((char *)xs + a.rg_off);  // [16 MB][rs]
+  float *hl = tl + PS * rs;                       // [16 MB][hs] (per-rank gate)
+  const int nst = (a.rank + 3) / 4;
+  // B for the first eight rank steps does not depend on the producers
+  float bv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = min(4 * min(i, nst - 1) + h, a.rank - 1);
+    bv[i] = to_f32<DT>(a.B[(size_t)row * a.rank + j]);
+  }
+  wait_producers(a, tid);
+  const __amdgpu_buffer_rsrc_t pr =
+      __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
+  const int kq = a.ks / 4;
+  const int E = a.M * rows;
+  // four elements per thread per round, their (up to 4 x 4) loads in flight together
+  for (int e0 = 0; e0 < E; e0 += 4 * kThreads) {
+    f32x4_t v[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + tid + kThreads * u;
+      const int m = e / rows, j = e - m * rows;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        v[u][qq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (e < E && qq < kq) v[u][qq] = load_partials4(pr, ((j * PS + m) * a.ks + 4 * qq) * 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + tid + kThreads * u;
+      if (e < E) {
+        const int m = e / rows, j = e - m * rows;
+        float t = 0.f;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          if (qq < kq) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t += v[u][qq][i];
+          }
+        tl[m * rs + j] = t;
+      }
+    }
+  }
+  __syncthreads();
+  if (a.rg_hidden > 0) {
+    for (int i = tid; i < a.M * a.rg_hidden; i += kThreads) {
+      const int m = i / a.rg_hidden, c = i - m * a.rg_hidden;
+      float v = a.rg_b1[c];
+      for (int k = 0; k < a.rank; ++k) v += a.rg_W1[(size_t)c * a.rank + k] * tl[m * rs + k];
+      hl[m * hs + c] = v > 0.f ? v : 0.f;
+    }
+    __syncthreads();
+    for (int i = tid; i < a.M * a.rank; i += kThreads) {
+      const int m = i / a.rank, j = i - m * a.rank;
+      float v = a.rg_b2[j];
+      for (int c = 0; c < a.rg_hidden; ++c) v += a.rg_W2[(size_t)j * a.rg_hidden + c] * hl[m * hs + c];
+      tl[m * rs + j] *= a.rg_alpha * gate_sigmoid(v);
+    }
+  } else {
+    // g from the gate row (column rank), which this pass does not overwrite
+    for (int i = tid; i < a.M * a.rank; i += kThreads) {
+      const int m = i / a.rank, j = i - m * a.rank;
+      tl[m * rs + j] *= gate_sigmoid(tl[m * rs + a.rank] + a.b_gate);
+    }
+  }
+  __syncthreads();
+  for (int st0 = 0; st0 < nst; st0 += 8) {
+    if (st0 > 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = min(4 * min(st0 + i, nst - 1) + h, a.rank - 1);
+        bv[i] = to_f32<DT>(a.B[(size_t)row * a.rank + j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = 4 * (st0 + i) + h;
+      if (st0 + i < nst) {
+        const bool jin = j < a.rank;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int m = col + 16 * mb;
+          acc[mb] = mfma_16x16x4_f32((jin && m < a.M) ? tl[m * rs + j] : 0.f, jin ? bv[i] : 0.f,
+                                     acc[mb]);
+        }
+      }
+    }
+  }
+}
+
+template <int DT, int MB, bool EC, bool PERCH>
+__device__ void consume_split(const DecodeArgs &a, int c, uint16_t *xs, int tid) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 15, h = lane >> 4;
+  const int q = c % a.ksp, tile = c / a.ksp;
+  const int n0 = tile * 16 * kWaves;
+  const int n = n0 + 16 * wave + col;
+  const int row = min(n, a.N - 1);
+  const uint32_t *wrow = a.qw + (size_t)row * (a.K / 8);
+  const int kb0 = q * a.nbs;                // the plan leaves no split empty
+  const int kb1 = min(a.nb, kb0 + a.nbs);
+  const int kx0 = kb0 * 128;                // first staged K column
+
+  uint32_t zc_row = 0;
+  float s_row = 0.f;
+  if constexpr (PERCH) {
+    zc_row = zero_constant<DT>(a.zeros[row]);
+    s_row = (float)bitcast<_Float16>(a.scales[row]);
+  }
+
+  u32x4_t wr_ring[kDepth];
+  auto wload = [&](int b, u32x4_t &w) {
+    const int kb = min(kb0 + b, kb1 - 1);
+    const int off = (kb * 128 + 32 * h < a.K) ? kb * 16 + 4 * h : 0;
+    w = __builtin_nontemporal_load((const u32x4_t *)(wrow + off));
+  };
+
+  // x columns [kx0, kx0 + nbs 128) of every token, in batches of 8 pieces per
+  // thread; columns past K are staged as zeros
+  const int per_row = a.nbs * 16;
+  const int total = a.M * per_row;
+  XBatch xb;
+  auto xload = [&](int p0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = min(p0 + tid + kThreads * i, total - 1);
+      const int m = p / per_row, j = p - m * per_row;
+      const int k = min(kx0 + 8 * j, a.K - 8);
+      xb.v[i] = *(const u32x4_t *)(a.x + (size_t)m * a.K + k);
+    }
+  };
+  auto xstore = [&](int p0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = p0 + tid + kThreads * i;
+      if (p < total) {
+        const int m = p / per_row, j = p - m * per_row;
+        const u32x4_t val = (kx0 + 8 * j < a.K) ? xb.v[i] : u32x4_t{0u, 0u, 0u, 0u};
+        *(u32x4_t *)(xs + m * a.xstr + 8 * j) = permute_8(val);
+      }
+    }
+  };
+
+  // scale/zero table of the split's groups g0 .. g0 + ngs - 1 for the tile's
+  // 128 rows: entry (r, gi) at 2 (r ngs + gi); at most 4 entries per thread
+  // (the plan checks 128 ngs <= 4 kThreads)
+  uint32_t *szs = (uint32_t *)((char *)xs + a.sz_off);
+  const int gpb = a.G / 128;  // 128-wide blocks per group (G a multiple of 128 here)
+  const int g0 = kb0 / gpb;
+  uint16_t sv[4], zv[4];
+  if constexpr (!PERCH) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + kThreads * u;
+      const int r = e / a.ngs, gi = e - r * a.ngs;
+      const int nr = min(n0 + r, a.N - 1), g = min(g0 + gi, a.ngroups - 1);
+      sv[u] = a.scales[(size_t)nr * a.ngroups + g];
+      zv[u] = a.zeros[(size_t)nr * a.ngroups + g];
+    }
+  }
+  xload(0);
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i) wload(i, wr_ring[i]);
+  if constexpr (!PERCH) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + kThreads * u;
+      if (e < 16 * kWaves * a.ngs) {
+        szs[2 * e] = zero_constant<DT>(zv[u]);
+        szs[2 * e + 1] = bitcast<uint32_t>((float)bitcast<_Float16>(sv[u]));
+      }
+    }
+  }
+  zero_strip(a, xs, tid);
+  xstore(0);
+  for (int p0 = kThreads * 8; p0 < total; p0 += kThreads * 8) {
+    xload(p0);
+    xstore(p0);
+  }
+  __syncthreads();
+
+  f32x4_t acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int szrow = 2 * (16 * wave + col) * a.ngs;
+  int xrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) xrow[mb] = min(col + 16 * mb, a.M - 1) * a.xstr;
+
+  auto group = [&](int b0, auto refill_tag) {
+    constexpr bool kRefill = decltype(refill_tag)::value;
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      const int b = b0 + i;
+      const u32x4_t w = wr_ring[i];
+      if constexpr (kRefill) wload(b + kDepth, wr_ring[i]);
+      const int kb = kb0 + b;
+      const bool live = kb < kb1;
+      uint32_t zc = zc_row;
+      float sc = 1.f;
+      if constexpr (!PERCH) {
+        const int g = (int)(((uint32_t)min(kb, kb1 - 1) * a.gmul) >> 20) - g0;
+        zc = szs[szrow + 2 * g];
+        sc = bitcast<float>(szs[szrow + 2 * g + 1]);
+      }
+      const int kloc = (live ? b * 128 : a.xzero) + 32 * h;
+      u32x4_t bop[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bop[t] = dequant_word<DT>(w[t], zc);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        u32x4_t aop[4];
+        const uint16_t *xp = xs + xrow[mb] + kloc;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) aop[t] = *(const u32x4_t *)(xp + 8 * t);
+        if constexpr (PERCH) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[mb] = mfma_16x16x32<DT>(aop[t], bop[t], acc[mb]);
+        } else {
+          const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t c0 = mfma_16x16x32<DT>(aop[0], bop[0], z4);
+          f32x4_t c1 = mfma_16x16x32<DT>(aop[2], bop[2], z4);
+          c0 = mfma_16x16x32<DT>(aop[1], bop[1], c0);
+          c1 = mfma_16x16x32<DT>(aop[3], bop[3], c1);
+          acc[mb] += sc * (c0 + c1);
+        }
+      }
+    }
+  };
+  const int last = a.nbw_pad - kDepth;
+  for (int b0 = 0; b0 < last; b0 += kDepth) group(b0, std::true_type{});
+  group(last, std::false_type{});
+
+  if constexpr (PERCH) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] *= s_row;
+  }
+
+  // publish this split's partial tile, then count it in
+  const __amdgpu_buffer_rsrc_t yr =
+      __builtin_amdgcn_make_buffer_rsrc(a.party, (short)0, a.party_bytes, 0x00020000);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    __builtin_amdgcn_raw_buffer_store_b128(bitcast<u32x4_t>(acc[mb]), yr,
+                                           split_piece_off<MB>(a, q, tile, wave, mb, lane), 0, 16);
+  publish_wait();
+  int *last_flag = (int *)((char *)xs + a.red_off);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&a.hdr->tile[tile].v, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    *last_flag = (old + 1 == (uint32_t)a.ksp) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*last_flag == 0) return;  // uniform: another split completes this tile
+
+  // the tile's sum over its splits, in split order (this split's own from registers)
+  f32x4_t v[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) v[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int q0 = 0; q0 < a.ksp; q0 += 8) {
+    f32x4_t pv[MB][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        pv[mb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // the tile's other splits only, no duplicates: uncached loads are costly per CU
+        if (q0 + i < a.ksp && q0 + i != q)
+          pv[mb][i] = load_partials4(yr, split_piece_off<MB>(a, q0 + i, tile, wave, mb, lane));
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (q0 + i < a.ksp) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) v[mb] += (q0 + i == q) ? acc[mb] : pv[mb][i];
+      }
+  }
+  if constexpr (EC) split_ec_epilogue<DT, MB>(a, xs, v, row, tid);
+  if (n < a.N) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * mb + 4 * h + e;
+        if (m < a.M) a.y[(size_t)m * a.N + n] = from_f32<DT>(v[mb][e]);
+      }
+  }
+  if (tid == 0)
+    __hip_atomic_store(&a.hdr->tile[tile].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Count this workgroup out; the last one resets the counters.  Workgroup b
@@ -655,6 +1018,54 @@ __global__ __launch_bounds__(kThreads, XMODE == XWHOLE ? 4 : 2) void decode_kern
   } else {
     consume<DT, MB, EC, PERCH, XMODE, WR>(a, b, xs, red, tid);
   }
+}
+
+template <int DT, int MB, bool EC, bool PERCH>
+__global__ __launch_bounds__(kThreads, 4) void decode_split_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) uint16_t xs[];
+  f32x4_t(*red)[MB][64] = (f32x4_t(*)[MB][64])((char *)xs + a.red_off);
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  if constexpr (EC) {
+    if (b < a.producers) {
+      produce<DT, MB>(a, b, red, tid >> 6, tid & 63);
+    } else {
+      consume_split<DT, MB, EC, PERCH>(a, b - a.producers, xs, tid);
+    }
+    if (tid == 0) finish(a);
+  } else {
+    consume_split<DT, MB, EC, PERCH>(a, b, xs, tid);
+  }
+}
+
+template <int DT, int MB, bool EC, bool PERCH>
+hipError_t launch_split_t(const DecodeArgs &a, int grid, size_t lds, hipStream_t s) {
+  auto kern = decode_split_kernel<DT, MB, EC, PERCH>;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   kMaxLds);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_split(const DecodeArgs &a, const DecodePlan &p, bool ec, bool perch,
+                        hipStream_t s) {
+  const int grid = p.n_tiles * p.ksp + p.producers;
+  if (p.mb == 1) {
+    if (ec) return perch ? launch_split_t<DT, 1, true, true>(a, grid, p.lds, s)
+                         : launch_split_t<DT, 1, true, false>(a, grid, p.lds, s);
+    return perch ? launch_split_t<DT, 1, false, true>(a, grid, p.lds, s)
+                 : launch_split_t<DT, 1, false, false>(a, grid, p.lds, s);
+  }
+  if (ec) return perch ? launch_split_t<DT, 2, true, true>(a, grid, p.lds, s)
+                       : launch_split_t<DT, 2, true, false>(a, grid, p.lds, s);
+  return perch ? launch_split_t<DT, 2, false, true>(a, grid, p.lds, s)
+               : launch_split_t<DT, 2, false, false>(a, grid, p.lds, s);
 }
 
 template <int DT, int MB, bool EC, bool PERCH, int XMODE, int WR>
@@ -804,9 +1215,87 @@ size_t decode_workspace_bytes(const LayerDesc &L, int M) {
   return kWsDataOff + (size_t)p.producers * 16 * (16 * p.mb) * sizeof(float);
 }
 
+// Split-K consumers are considered from this many tokens on and for K of at
+// least this many columns (process-wide).  Below K = 8192 a split's tail (its
+// partial tile stored, the tile's arrival counted, the partials gathered:
+// three memory round trips, about 3.5 us on MI355X) is not paid back by the
+// shorter K loop (measured at M = 16 and 32 on the 4096-wide projections).
+static std::atomic<int> g_split_min_m{16};
+static std::atomic<int> g_split_min_k{8192};
+void set_decode_split_min_m(int m) { g_split_min_m.store(m); }
+int get_decode_split_min_m() { return g_split_min_m.load(); }
+void set_decode_split_min_k(int k) { g_split_min_k.store(k); }
+int get_decode_split_min_k() { return g_split_min_k.load(); }
+
+
+// The split-K launch: 128-row tiles (one 16-row block per wave) and the most
+// K-splits, at most 8, with which every workgroup (producers included) is
+// resident at once.  ok == false when no split of at least 2 fits: too many
+// tiles, too little K, or the LDS.
+DecodePlan plan_decode_split(const LayerDesc &L, int M) {
+  DecodePlan p{};
+  p.ok = false;
+  p.mb = M <= 16 ? 1 : 2;
+  p.rb_a = L.rank > 0 ? (L.rank + L.gate_rows() + 15) / 16 : 0;
+  p.ks = L.rank > 0 ? decode_ksplit(L.K) : 0;
+  p.producers = p.rb_a * p.ks;
+  p.nb = (L.K + 127) / 128;
+  p.wr = kWaves;
+  p.n_tiles = (L.N + 16 * kWaves - 1) / (16 * kWaves);
+  if (p.n_tiles > kMaxSplitTiles || p.nb < 2 || L.K < g_split_min_k.load()) return p;
+  const int gpb = L.per_channel ? 1 : L.G / 128;
+  for (int want = 8; want >= 2; --want) {
+    DecodePlan c = p;
+    c.nbs = (c.nb + want - 1) / want;
+    c.ksp = (c.nb + c.nbs - 1) / c.nbs;  // every split non-empty
+    if (c.ksp < 2) continue;
+    c.ngs = L.per_channel ? 0 : (c.nbs - 1) / gpb + 2;
+    if (!L.per_channel && 16 * kWaves * c.ngs > 4 * kThreads) continue;
+    c.xmode = XWHOLE;
+    c.xzero = c.nbs * 128;
+    c.xstr = c.xzero + 128 + 8;
+    c.nbw = c.nbs;
+    c.nbw_pad = (c.nbs + kDepth - 1) / kDepth * kDepth;
+    c.lds = (size_t)M * c.xstr * 2;
+    c.sz_off = (int)((c.lds + 15) / 16 * 16);
+    c.lds = c.sz_off + (size_t)16 * kWaves * c.ngs * 8;
+    c.red_off = (int)((c.lds + 15) / 16 * 16);
+    c.lds = c.red_off + (size_t)kWaves * c.mb * 64 * 16;
+    c.rg_off = (int)((c.lds + 15) / 16 * 16);
+    if (L.rank > 0) c.lds = c.rg_off + (size_t)16 * c.mb * (L.rank + 1 + L.rg_hidden + 1) * sizeof(float);
+    if (c.lds > (size_t)kMaxLds) continue;
+    const int by_lds = (int)((size_t)kMaxLds / c.lds);
+    const int resident = by_lds < 2 ? by_lds : 2;  // 8-wave workgroups at 4 waves per SIMD
+    if (c.n_tiles * c.ksp + c.producers > 256 * resident) continue;
+    const size_t ec_bytes = (size_t)c.producers * 16 * (16 * c.mb) * sizeof(float);
+    c.split_off = kWsDataOff + (ec_bytes + 255) / 256 * 256;
+    c.split_bytes = (size_t)c.ksp * c.n_tiles * kWaves * c.mb * 64 * 16;
+    c.ok = true;
+    return c;
+  }
+  return p;
+}
+
+// The split-K launch is taken for M >= the threshold when its plan fits and
+// the workspace holds its partial tiles.
+static bool use_split(const DecodePlan &sp, int M, size_t ws_bytes) {
+  return sp.ok && M >= g_split_min_m.load() && ws_bytes >= sp.split_off + sp.split_bytes;
+}
+
+size_t decode_fast_workspace_bytes(const LayerDesc &L, int M) {
+  size_t need = decode_workspace_bytes(L, M);
+  if (M >= g_split_min_m.load()) {
+    const DecodePlan sp = plan_decode_split(L, M);
+    if (sp.ok && sp.split_off + sp.split_bytes > need) need = sp.split_off + sp.split_bytes;
+  }
+  return need;
+}
+
 hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
-                         void *ws, hipStream_t s) {
-  const DecodePlan p = plan_decode(L, M);
+                         void *ws, size_t ws_bytes, hipStream_t s) {
+  const DecodePlan sp = plan_decode_split(L, M);
+  const bool split = ws && use_split(sp, M, ws_bytes);
+  const DecodePlan p = split ? sp : plan_decode(L, M);
   if (!p.ok) return hipErrorInvalidConfiguration;
   DecodeArgs a{};
   a.qw = L.qw;
@@ -850,6 +1339,15 @@ hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint1
   a.hdr = (WsHeader *)ws;
   a.part = ws ? (float *)((char *)ws + kWsDataOff) : nullptr;
   const bool ec = L.rank > 0;
+  if (split) {
+    a.ksp = p.ksp;
+    a.nbs = p.nbs;
+    a.ngs = p.ngs;
+    a.party_bytes = (int)p.split_bytes;
+    a.party = (float *)((char *)ws + p.split_off);
+    return dtype == DT_F16 ? launch_split<DT_F16>(a, p, ec, L.per_channel, s)
+                           : launch_split<DT_BF16>(a, p, ec, L.per_channel, s);
+  }
   return dtype == DT_F16 ? launch_mb<DT_F16>(a, p, ec, L.per_channel, s)
                          : launch_mb<DT_BF16>(a, p, ec, L.per_channel, s);
 }

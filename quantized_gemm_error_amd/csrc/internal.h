@@ -16,7 +16,11 @@ struct alignas(128) WsCounter {
   uint32_t pad[31];
 };
 
-// Workspace header: the first 2048 bytes of every workspace.  Zeroed once by
+// Output tiles (128 rows each) of the split-K decode launch: one arrival
+// counter each in the header.
+constexpr int kMaxSplitTiles = 128;
+
+// Workspace header: the first 18432 bytes of every workspace.  Zeroed once by
 // the caller; each decode launch that uses it leaves the counters at zero.
 struct WsHeader {
   WsCounter arrive;    // compensator producers that published their partials
@@ -24,8 +28,9 @@ struct WsHeader {
   WsCounter done_top;  // slots of finished workgroups that are complete
   WsCounter done[8];   // finished workgroups, by blockIdx % 8
   WsCounter pad[5];
+  WsCounter tile[kMaxSplitTiles];  // split-K decode: K-splits of each output tile that are in
 };
-static_assert(sizeof(WsHeader) == 2048, "workspace header is 2048 bytes");
+static_assert(sizeof(WsHeader) == 2048 + 128 * kMaxSplitTiles, "workspace header size");
 
 // The header holds every counter a call relies on finding at zero; from
 // kWsDataOff on, every byte a call reads it has written itself first, so one
@@ -68,17 +73,27 @@ struct DecodePlan {
   int red_off;     // byte offset of the wave-reduction buffer in dynamic LDS
   int rg_off;      // per-rank gate scratch (0 when the layer has none)
   size_t lds;      // dynamic LDS bytes
+  // split-K consumers (ksp > 1): ksp K-splits of nbs blocks for each 128-row
+  // tile; their fp32 partial tiles start at split_off in the workspace
+  int ksp, nbs, ngs;
+  size_t split_off, split_bytes;
 };
 
 DecodePlan plan_decode(const LayerDesc &L, int M);
+DecodePlan plan_decode_split(const LayerDesc &L, int M);  // ok == false: no split launch
 bool decode_supported(const LayerDesc &L, int M);
-size_t decode_workspace_bytes(const LayerDesc &L, int M);
+size_t decode_workspace_bytes(const LayerDesc &L, int M);       // required
+size_t decode_fast_workspace_bytes(const LayerDesc &L, int M);  // enough for the split-K launch
+void set_decode_split_min_m(int m);
+int get_decode_split_min_m();
+void set_decode_split_min_k(int k);
+int get_decode_split_min_k();
 size_t prefill_workspace_bytes(const LayerDesc &L, int M);
 bool prefill_needs_workspace(const LayerDesc &L);  // false: optional (splits K when given)
 
 hipError_t launch_pack_int4(const uint8_t *q, int32_t *out, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
-                         void *ws, hipStream_t s);
+                         void *ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
                           void *ws, hipStream_t main_s, hipStream_t aux_s);
 

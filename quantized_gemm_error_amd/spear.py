@@ -28,7 +28,9 @@ SPEAR_MAX_DECODE_M = 32
 # Every function the header declares, for the export check.
 EXPORTED = (
     "spear_workspace_bytes", "spear_pack_int4", "spear_linear_decode", "spear_linear_prefill",
-    "spear_linear", "spear_set_decode_max_m", "spear_get_decode_max_m", "spear_select_chunk",
+    "spear_linear", "spear_set_decode_max_m", "spear_get_decode_max_m",
+    "spear_set_decode_split_min_m", "spear_get_decode_split_min_m",
+    "spear_set_decode_split_min_k", "spear_get_decode_split_min_k", "spear_select_chunk",
     "spear_status_string", "spear_last_error", "spear_workspace_flags", "spear_version",
 )
 
@@ -86,6 +88,14 @@ def load_library(path: str = LIB_PATH):
     lib.spear_set_decode_max_m.restype = i32
     lib.spear_get_decode_max_m.argtypes = []
     lib.spear_get_decode_max_m.restype = i32
+    lib.spear_set_decode_split_min_m.argtypes = [i32]
+    lib.spear_set_decode_split_min_m.restype = i32
+    lib.spear_get_decode_split_min_m.argtypes = []
+    lib.spear_get_decode_split_min_m.restype = i32
+    lib.spear_set_decode_split_min_k.argtypes = [i32]
+    lib.spear_set_decode_split_min_k.restype = i32
+    lib.spear_get_decode_split_min_k.argtypes = []
+    lib.spear_get_decode_split_min_k.restype = i32
     lib.spear_select_chunk.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float), i32,
                                        ctypes.c_float, ctypes.POINTER(i32)]
     lib.spear_select_chunk.restype = i32
@@ -243,6 +253,22 @@ def spear_set_decode_max_m(m: int) -> None:
 
 def spear_get_decode_max_m() -> int:
     return int(load_library().spear_get_decode_max_m())
+
+
+def spear_set_decode_split_min_m(m: int) -> None:
+    _check(load_library().spear_set_decode_split_min_m(int(m)))
+
+
+def spear_get_decode_split_min_m() -> int:
+    return int(load_library().spear_get_decode_split_min_m())
+
+
+def spear_set_decode_split_min_k(k: int) -> None:
+    _check(load_library().spear_set_decode_split_min_k(int(k)))
+
+
+def spear_get_decode_split_min_k() -> int:
+    return int(load_library().spear_get_decode_split_min_k())
 
 
 def spear_select_chunk(chunks, pred_ms, budget_ms: float):

@@ -79,6 +79,26 @@ def test_decode_max_m_setting(lib):
     assert spear.spear_get_decode_max_m() == 32
 
 
+def test_decode_split_min_m_setting(lib):
+    assert spear.spear_get_decode_split_min_m() == 16
+    assert spear.spear_get_decode_split_min_k() == 8192
+    spear.spear_set_decode_split_min_k(1)
+    assert spear.spear_get_decode_split_min_k() == 1
+    spear.spear_set_decode_split_min_k(8192)
+    with pytest.raises(spear.SpearError):
+        spear.spear_set_decode_split_min_k(0)
+    spear.spear_set_decode_split_min_m(33)  # never split
+    assert spear.spear_get_decode_split_min_m() == 33
+    spear.spear_set_decode_split_min_m(1)
+    assert spear.spear_get_decode_split_min_m() == 1
+    spear.spear_set_decode_split_min_m(16)
+    with pytest.raises(spear.SpearError):
+        spear.spear_set_decode_split_min_m(0)
+    with pytest.raises(spear.SpearError):
+        spear.spear_set_decode_split_min_m(34)
+    assert spear.spear_get_decode_split_min_m() == 16
+
+
 FAKE = 0x10000  # 64 KiB-aligned fake device address: validation never dereferences it
 
 

@@ -6,6 +6,7 @@ rank-0 layer.  Small shapes are compared in full (several tiles plus ragged
 tails in N, M and K); the Llama-shaped layers on sampled output rows.
 """
 
+import contextlib
 import json
 import os
 
@@ -34,10 +35,29 @@ def _setup(N, K, G, r, seed, dtype="f16", M=1, outliers=False, **kw):
     return hl, x_bits, lay, x
 
 
+WS_HEADER_BYTES = 2048 + 128 * 128  # 16 counter lines, then 128 split-K tile counters
+
+
 def _ws_header(ws):
-    """Workspace counters (arrive, flags, done_top, done[0..7]); one per 128-byte line."""
-    words = ws[:2048].view(torch.int32).cpu().tolist()
-    return [words[32 * i] for i in range(11)]
+    """Workspace counters (arrive, flags, done_top, done[0..7]) and whether every
+    split-K tile counter is back at zero; one counter per 128-byte line."""
+    words = ws[:WS_HEADER_BYTES].view(torch.int32).cpu().tolist()
+    tiles = [words[32 * (16 + i)] for i in range(128)]
+    return [words[32 * i] for i in range(11)] + [int(any(tiles))]
+
+
+@contextlib.contextmanager
+def decode_split_min_m(m):
+    """Run the block with the decode split-K threshold at m tokens (33: never split)
+    and at any K."""
+    old = spear.spear_get_decode_split_min_m(), spear.spear_get_decode_split_min_k()
+    spear.spear_set_decode_split_min_m(m)
+    spear.spear_set_decode_split_min_k(1)
+    try:
+        yield
+    finally:
+        spear.spear_set_decode_split_min_m(old[0])
+        spear.spear_set_decode_split_min_k(old[1])
 
 
 # ---------------------------------------------------------------------------
@@ -106,16 +126,21 @@ DECODE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("split_min", [1, 33], ids=["split", "unsplit"])
 @pytest.mark.parametrize("N,K,G,r,M,dtype,outl", DECODE_CASES)
-def test_decode_parity(N, K, G, r, M, dtype, outl):
-    note(f"decode N={N} K={K} G={G} r={r} M={M} {dtype}")
+def test_decode_parity(N, K, G, r, M, dtype, outl, split_min):
+    note(f"decode N={N} K={K} G={G} r={r} M={M} {dtype} split_min={split_min}")
     hl, xb, lay, x = _setup(N, K, G, r, seed=N + K + r + M, dtype=dtype, M=M, outliers=outl,
                             b_gate=0.25)
-    ws = spear.new_workspace(lay, M)
-    y = spear.spear_linear_decode(lay, x, workspace=ws)
+    with decode_split_min_m(split_min):
+        ws = spear.new_workspace(lay, M)
+        y = spear.spear_linear_decode(lay, x, workspace=ws)
+        y0 = spear.spear_linear_decode(lay.without_compensator(), x,
+                                       workspace=spear.new_workspace(lay.without_compensator(), M))
     torch.cuda.synchronize()
     assert_close(gpu_y_f64(y, dtype), oracle_y(hl, xb), f"decode {N}x{K} M={M}")
-    assert _ws_header(ws) == [0] * 11
+    assert_close(gpu_y_f64(y0, dtype), oracle_y(hl, xb, with_ec=False), f"decode r=0 {N}x{K} M={M}")
+    assert _ws_header(ws) == [0] * 12
 
 
 @pytest.mark.parametrize("M", [1, 4, 16, 32])
@@ -126,7 +151,9 @@ def test_decode_gate_off_is_rank_zero_bitwise(M):
     lay.b_gate = float("-inf")
     ws = spear.new_workspace(lay, M)
     y_off = spear.spear_linear_decode(lay, x, workspace=ws)
-    y_r0 = spear.spear_linear_decode(lay.without_compensator(), x)
+    # the same launch shape (split-K from 16 tokens on, given the workspace) at rank 0
+    lay0 = lay.without_compensator()
+    y_r0 = spear.spear_linear_decode(lay0, x, workspace=spear.new_workspace(lay0, M))
     torch.cuda.synchronize()
     assert torch.equal(y_off.view(torch.int16), y_r0.view(torch.int16))
     assert_close(gpu_y_f64(y_r0, "f16"), oracle_y(hl, xb, with_ec=False), "rank 0")
@@ -296,7 +323,7 @@ def test_decode_workspace_reuse_many_calls():
     for (it, M), y in outs.items():
         assert_close(gpu_y_f64(y, "f16"), ref[:M], f"call {it} M={M}")
     assert spear.spear_workspace_flags(ws) == 0
-    assert _ws_header(ws) == [0] * 11
+    assert _ws_header(ws) == [0] * 12
 
 
 def test_decode_fresh_inputs_every_call():
@@ -315,7 +342,7 @@ def test_decode_fresh_inputs_every_call():
     for it, xb, y in cases:
         assert_close(gpu_y_f64(y, "f16"), oracle_y(hl, xb), f"call {it}")
     assert spear.spear_workspace_flags(ws) == 0
-    assert _ws_header(ws) == [0] * 11
+    assert _ws_header(ws) == [0] * 12
 
 
 # ---------------------------------------------------------------------------
