@@ -49,7 +49,10 @@ constexpr int BM = 128, BN = 128, BK = 128;
 // fragment read puts 16 rows x 2 column groups in flight; a 288-byte stride
 // spreads them over distinct banks.  Measured at M = 2048 (bf16, rank 0):
 // padding by 16 halves runs the GEMM 6-7% faster than by 8 or 24, and by 40
-// or 48 costs the second workgroup per CU.
+// or 48 costs the second workgroup per CU.  (An unpadded layout with an XOR
+// swizzle that also frees the tile stores of conflicts ran 10% slower, most
+// likely because its per-lane addresses replace the LDS instructions'
+// immediate offsets in a kernel already near its register budget.)
 constexpr int LSTR = BK + 16;
 constexpr int WSTR = BK + 16;
 
@@ -118,7 +121,9 @@ struct GemmArgs {
 };
 
 constexpr int kEpiRc = 32;           // ranks per epilogue chunk: the K of one 16x16x32 MFMA
-constexpr int kEpiStr = kEpiRc + 8;  // LDS row stride of a chunk's bf16 operands (halves)
+// LDS row stride of a chunk's bf16 operands (halves): 24 dwords, so a
+// fragment read's 16 rows x 2 column groups fall on distinct banks
+constexpr int kEpiStr = kEpiRc + 16;
 static_assert(2 * BM * kEpiStr <= BM * LSTR, "epilogue U hi/lo fit the activation tile");
 static_assert(2 * BN * kEpiStr <= BN * WSTR, "epilogue B hi/lo fit the weight tile");
 
