@@ -439,6 +439,10 @@ struct EcArgs {
   const uint16_t *x, *A, *wg;
   int K, M, rank, rows, rp1, ks;  // rows of [A; w_g]: rank + 1, or rank (per-rank gate)
   float *Tp;  // [ks][M][rp1]
+  // ks == 1 with the scalar gate: U = diag(g) (X A^T) written here directly
+  // (zeros in columns rank .. rp1-1), and no partials
+  float *U;
+  float b_gate;
 };
 
 constexpr int kEcWaves = 8, kEcRb = 3, kEcU = 4, kEcTok = 32, kEcMb = kEcTok / 16;
@@ -531,6 +535,17 @@ __global__ __launch_bounds__(64 * kEcWaves) void prefill_ec_kernel(EcArgs a) {
   }
 
 
+  if (a.U) {
+    // the whole of K in this workgroup: U = g t for its tokens, g from row rank
+    const int nval = kEcTok * a.rp1;
+    for (int i = tid; i < nval; i += 64 * kEcWaves) {
+      const int mm = i / a.rp1, j = i - mm * a.rp1;
+      if (m0 + mm < a.M)
+        a.U[(size_t)(m0 + mm) * a.rp1 + j] =
+            j < a.rank ? gate_sigmoid(tz[mm][a.rank] + a.b_gate) * tz[mm][j] : 0.f;
+    }
+    return;
+  }
   // this split's sums, rows 0..rows-1 of its tokens
   const int nval = kEcTok * a.rows;
   float *tp = a.Tp + ((size_t)ksi * a.M + m0) * a.rp1;
@@ -905,7 +920,8 @@ hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint
   if (ec) {
     const int rp1 = rank_pad(L.rank + 1);
     eks = ec_ksplit(M, L.K);
-    ea = EcArgs{x, L.A, L.wg, L.K, M, L.rank, L.rank + L.gate_rows(), rp1, eks, (float *)(base + w.tp)};
+    ea = EcArgs{x, L.A, L.wg, L.K, M, L.rank, L.rank + L.gate_rows(), rp1, eks, (float *)(base + w.tp),
+                (eks == 1 && !rgate) ? (float *)(base + w.ts) : nullptr, L.b_gate};
     // consumers read U, formed once from the split partials
     uv = UView{(const float *)(base + w.ts), M, L.rank, rp1};
   }
@@ -933,6 +949,7 @@ hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint
       hipLaunchKernelGGL(prefill_rgate_kernel, dim3((M + kRgTok - 1) / kRgTok), dim3(256), 0, s, ra);
       return hipGetLastError();
     }
+    if (ea.U) return hipSuccess;  // U written by the compensator kernel
     const UArgs ua{ea.Tp, (float *)(base + w.ts), eks, M, L.rank, ea.rp1, L.b_gate};
     const int n = M * (ea.rp1 / 4);
     hipLaunchKernelGGL(prefill_u_kernel, dim3((n + 255) / 256), dim3(256), 0, s, ua);

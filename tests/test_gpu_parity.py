@@ -357,6 +357,7 @@ PREFILL_CASES = [
     (384, 768, 256, 32, 257, "bf16", True, True),  # G = 256, bf16
     (128, 256, 128, 0, 100, "f16", False, True),   # rank 0
     (64, 128, 128, 4, 33, "f16", False, True),     # M just above the decode range
+    (160, 256, 128, 32, 300, "bf16", True, False), # K < 512: one compensator split forms U itself
     (200, 512, 128, 100, 77, "f16", False, True),  # rank 100: padded U rows, 7 row blocks of [A; w_g]
     (256, 4096, 128, 32, 100, "f16", True, False),  # 2 output tiles: K split 8 ways, serial
     (136, 4096, 0, 16, 40, "bf16", True, False),    # K split, per-channel, ragged N
