@@ -104,6 +104,23 @@ __device__ __forceinline__ u32x4_t dequant_word(uint32_t w, uint32_t zc) {
   return r;
 }
 
+// bf16 only: one packed word to the exact values q_i - z in natural order,
+// four dwords holding (q0,q1) (q2,q3) (q4,q5) (q6,q7).  Each nibble is
+// extracted on its own (as in dequant_word's bf16 form), so the order costs
+// nothing here, and the activation operand it meets needs no permutation.
+__device__ __forceinline__ u32x4_t dequant_word_bf16_natural(uint32_t w, uint32_t zc) {
+  const float zf = bitcast<float>(zc);
+  u32x4_t r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float lo = bitcast<float>(((w >> (8 * t)) & 0xFu) | 0x4B000000u) - zf;
+    const float hi = bitcast<float>(((w >> (8 * t + 4)) & 0xFu) | 0x4B000000u) - zf;
+    const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+    r[t] = bitcast<uint32_t>(p);
+  }
+  return r;
+}
+
 // Eight consecutive activation values (natural order) to the order
 // (x0,x4,x1,x5,x2,x6,x3,x7) that matches dequant_word's pairs.
 __device__ __forceinline__ u32x4_t permute_8(u32x4_t v) {

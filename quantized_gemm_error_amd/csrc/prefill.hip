@@ -199,7 +199,8 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
     for (int i = 0; i < 8; ++i) {
       const int p = tid + 256 * i;
       const int r = p >> 4, j8 = p & 15;
-      *(u32x4_t *)(xs + r * LSTR + 8 * j8) = permute_8(xr[i]);
+      // fp16 weights come in dequant_word's pair order, bf16 in natural order
+      *(u32x4_t *)(xs + r * LSTR + 8 * j8) = DT == DT_F16 ? permute_8(xr[i]) : xr[i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -208,7 +209,8 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
       const uint32_t zc = zero_constant<DT>(zr[i]);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        *(u32x4_t *)(wsm + r * WSTR + 32 * q4 + 8 * t) = dequant_word<DT>(wr[i][t], zc);
+        *(u32x4_t *)(wsm + r * WSTR + 32 * q4 + 8 * t) =
+            DT == DT_F16 ? dequant_word<DT>(wr[i][t], zc) : dequant_word_bf16_natural(wr[i][t], zc);
     }
     if (!PERCH && tid < BN) ss[tid] = (float)bitcast<_Float16>(sv);
   };
