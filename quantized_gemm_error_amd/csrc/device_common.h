@@ -104,18 +104,33 @@ __device__ __forceinline__ u32x4_t dequant_word(uint32_t w, uint32_t zc) {
   return r;
 }
 
+// The four bytes of x as fp32 (exact), one v_cvt_f32_ubyteN each.
+__device__ __forceinline__ void cvt_f32_ubytes(uint32_t x, float (&f)[4]) {
+  asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f[0]) : "v"(x));
+  asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f[1]) : "v"(x));
+  asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f[2]) : "v"(x));
+  asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f[3]) : "v"(x));
+}
+
 // bf16 only: one packed word to the exact values q_i - z in natural order,
 // four dwords holding (q0,q1) (q2,q3) (q4,q5) (q6,q7).  Each nibble is
 // extracted on its own (as in dequant_word's bf16 form), so the order costs
 // nothing here, and the activation operand it meets needs no permutation.
+// The even nibbles and the odd ones go to the bytes of two words, and each
+// byte converts to fp32 exactly (v_cvt_f32_ubyteN); q - z is then one exact
+// fp32 subtraction (z = zc's 2^23 + z less 2^23, exact) and one rounding-free
+// conversion of the integer pair to bf16.
 __device__ __forceinline__ u32x4_t dequant_word_bf16_natural(uint32_t w, uint32_t zc) {
-  const float zf = bitcast<float>(zc);
+  const float z = bitcast<float>(zc) - 8388608.0f;
+  const uint32_t ev = w & 0x0F0F0F0Fu;         // nibbles 0, 2, 4, 6
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // nibbles 1, 3, 5, 7
+  float fe[4], fo[4];
+  cvt_f32_ubytes(ev, fe);
+  cvt_f32_ubytes(od, fo);
   u32x4_t r;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const float lo = bitcast<float>(((w >> (8 * t)) & 0xFu) | 0x4B000000u) - zf;
-    const float hi = bitcast<float>(((w >> (8 * t + 4)) & 0xFu) | 0x4B000000u) - zf;
-    const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+    const bf16x2_t p = {(__bf16)(fe[t] - z), (__bf16)(fo[t] - z)};
     r[t] = bitcast<uint32_t>(p);
   }
   return r;

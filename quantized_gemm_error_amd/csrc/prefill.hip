@@ -171,7 +171,35 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
   uint16_t zr[2];
   uint16_t sv = 0;
 
-  auto gload = [&](int kb) {
+  // Loads of k-block kb.  Over the tile's rows, buffer resources return zeros
+  // past M (x) and past N (weights, zero-points, scales), every per-lane
+  // offset is loop-invariant, and the k-block's advance goes into the
+  // scalar offset.  The scalar offset is not range-checked, so a k-block
+  // that runs past K (K % 128 != 0) takes the guarded loads instead.
+  const int mrows = min(BM, a.M - m0), nrows = min(BN, a.N - n0);
+  const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.x + (size_t)m0 * a.K), (short)0, mrows * a.K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.qw + (size_t)n0 * kw), (short)0, nrows * kw * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t z_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.zeros + (size_t)n0 * a.ngroups), (short)0, nrows * a.ngroups * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.scales + (size_t)n0 * a.ngroups), (short)0, nrows * a.ngroups * 2, 0x00020000);
+  int x_off[8], w_off[2], z_off[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = tid + 256 * i;
+    x_off[i] = ((p >> 4) * a.K + 8 * (p & 15)) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + 256 * i;
+    w_off[i] = ((p >> 2) * kw + 4 * (p & 3)) * 4;
+    z_off[i] = (p >> 2) * a.ngroups * 2;
+  }
+  const int s_off = tid * a.ngroups * 2;
+
+  auto gload_guarded = [&](int kb) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int p = tid + 256 * i;
@@ -193,6 +221,23 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
     }
     if (!PERCH && tid < BN) sv = a.scales[(size_t)min(n0 + tid, a.N - 1) * a.ngroups + g];
   };
+  auto gload = [&](int kb) {
+    if (kb * BK + BK > a.K) {  // uniform
+      gload_guarded(kb);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, x_off[i], kb * BK * 2, 0);
+    const int g = PERCH ? 0 : min((kb * BK) / a.G, a.ngroups - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      wr[i] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off[i], kb * 64, 0);
+      zr[i] = __builtin_amdgcn_raw_buffer_load_b16(z_rs, z_off[i], g * 2, 0);
+    }
+    if (!PERCH && tid < BN) sv = __builtin_amdgcn_raw_buffer_load_b16(s_rs, s_off, g * 2, 0);
+  };
+
 
   auto lstore = [&]() {
 #pragma unroll
