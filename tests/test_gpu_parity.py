@@ -203,6 +203,10 @@ RANK_GATE_CASES = [
     ("prefill", 264, 1024, 128, 32, 16, 70, "f16", 0.7),
     ("prefill", 128, 4096, 128, 16, 32, 40, "bf16", 0.5),   # K split, many compensator splits
     ("prefill_aux", 200, 1024, 0, 32, 16, 150, "f16", 1.0),
+    # the split-K decode launch (forced at any M and K): its epilogue gathers t into LDS
+    ("decode_split", 200, 1024, 128, 32, 16, 1, "f16", 0.7),
+    ("decode_split", 96, 512, 128, 40, 64, 32, "f16", 1.0),
+    ("decode_split", 300, 2048, 0, 24, 8, 17, "bf16", 1.3),
 ]
 
 
@@ -225,6 +229,10 @@ def test_rank_gate_parity(path, N, K, G, r, hidden, M, dtype, alpha):
     ws = spear.new_workspace(lay, M)
     if path == "decode":
         y = spear.spear_linear_decode(lay, x, workspace=ws)
+    elif path == "decode_split":
+        with decode_split_min_m(1):
+            ws = spear.new_workspace(lay, M)
+            y = spear.spear_linear_decode(lay, x, workspace=ws)
     elif path == "prefill":
         y = spear.spear_linear_prefill(lay, x, workspace=ws)
     else:
@@ -324,6 +332,24 @@ def test_decode_workspace_reuse_many_calls():
         assert_close(gpu_y_f64(y, "f16"), ref[:M], f"call {it} M={M}")
     assert spear.spear_workspace_flags(ws) == 0
     assert _ws_header(ws) == [0] * 12
+
+
+def test_decode_split_needs_room_in_the_workspace():
+    """K >= 8192 at 16 tokens takes the split-K launch when the workspace holds its
+    partial tiles, and the unsplit launch with a workspace sized for one token; both
+    match the oracle."""
+    note("decode split-K fallback on a small workspace")
+    hl, xb, lay, x = _setup(256, 8192, 128, 32, seed=61, M=16, outliers=True)
+    ref = oracle_y(hl, xb)
+    big = spear.new_workspace(lay, 16)
+    small = spear.new_workspace(lay, 1)
+    assert small.numel() < big.numel()
+    y_split = spear.spear_linear_decode(lay, x, workspace=big)
+    y_plain = spear.spear_linear_decode(lay, x, workspace=small)
+    torch.cuda.synchronize()
+    assert_close(gpu_y_f64(y_split, "f16"), ref, "split")
+    assert_close(gpu_y_f64(y_plain, "f16"), ref, "unsplit")
+    assert _ws_header(big) == [0] * 12 and _ws_header(small) == [0] * 12
 
 
 def test_decode_fresh_inputs_every_call():
