@@ -619,6 +619,9 @@ def cpu_baseline(budget_s=12.0):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_llama7b_traffic.json")
 DOMINANT_SOURCES = ("quantized_gemm_error_amd/csrc/decode.hip",
+                    "quantized_gemm_error_amd/csrc/decode_impl.inc",
+                    "quantized_gemm_error_amd/csrc/decode_w8.hip",
+                    "quantized_gemm_error_amd/csrc/decode_w4.hip",
                     "quantized_gemm_error_amd/csrc/device_common.h",
                     "quantized_gemm_error_amd/csrc/internal.h")
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o run -- "

@@ -79,8 +79,8 @@ struct DecodePlan {
   size_t split_off, split_bytes;
 };
 
-DecodePlan plan_decode(const LayerDesc &L, int M);
-DecodePlan plan_decode_split(const LayerDesc &L, int M);  // ok == false: no split launch
+// Decode, dispatched per call to one of two compilations of the same kernels
+// (8 or 4 waves per workgroup; decode.hip picks).
 bool decode_supported(const LayerDesc &L, int M);
 size_t decode_workspace_bytes(const LayerDesc &L, int M);       // required
 size_t decode_fast_workspace_bytes(const LayerDesc &L, int M);  // enough for the split-K launch
@@ -88,6 +88,18 @@ void set_decode_split_min_m(int m);
 int get_decode_split_min_m();
 void set_decode_split_min_k(int k);
 int get_decode_split_min_k();
+
+#define SPEAR_DECODE_VARIANT_API                                                          \
+  DecodePlan plan_decode(const LayerDesc &L, int M);                                      \
+  DecodePlan plan_decode_split(const LayerDesc &L, int M); /* ok == false: no split */    \
+  bool decode_supported(const LayerDesc &L, int M);                                       \
+  size_t decode_workspace_bytes(const LayerDesc &L, int M);                               \
+  size_t decode_fast_workspace_bytes(const LayerDesc &L, int M);                          \
+  hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, \
+                           int M, void *ws, size_t ws_bytes, hipStream_t s);
+namespace w8 { SPEAR_DECODE_VARIANT_API }
+namespace w4 { SPEAR_DECODE_VARIANT_API }
+#undef SPEAR_DECODE_VARIANT_API
 size_t prefill_workspace_bytes(const LayerDesc &L, int M);
 bool prefill_needs_workspace(const LayerDesc &L);  // false: optional (splits K when given)
 
