@@ -912,7 +912,7 @@ def main():
         summarize_prefill_profiles(*args.summarize_prefill_profiles, out_dir=os.path.join(ROOT, "profiles"))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
