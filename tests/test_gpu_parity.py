@@ -383,6 +383,8 @@ PREFILL_CASES = [
     (384, 768, 256, 32, 257, "bf16", True, True),  # G = 256, bf16
     (128, 256, 128, 0, 100, "f16", False, True),   # rank 0
     (64, 128, 128, 4, 33, "f16", False, True),     # M just above the decode range
+    (96, 1024, 128, 8, 1, "f16", True, False),     # one token: one output tile, K split 2 ways, compensator 4
+    (96, 1024, 0, 16, 16, "bf16", False, True),    # 16 tokens, per-channel, concurrent schedule
     (160, 256, 128, 32, 300, "bf16", True, False), # K < 512: one compensator split forms U itself
     (200, 512, 128, 100, 77, "f16", False, True),  # rank 100: padded U rows, 7 row blocks of [A; w_g]
     (256, 4096, 128, 32, 100, "f16", True, False),  # 2 output tiles: K split 8 ways, serial
