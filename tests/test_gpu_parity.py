@@ -123,6 +123,7 @@ DECODE_CASES = [
     (200, 768, 128, 16, 7, "bf16", True),    # bf16
     (48, 8192, 0, 4, 2, "bf16", False),      # long K, several staged chunks at M = 2
     (33, 96, 0, 1, 1, "f16", False),         # rank 1, tiny K
+    (1, 32, 0, 2, 2, "f16", False),          # one output row, the smallest K (one 32-wide piece)
 ]
 
 
@@ -385,6 +386,7 @@ PREFILL_CASES = [
     (64, 128, 128, 4, 33, "f16", False, True),     # M just above the decode range
     (96, 1024, 128, 8, 1, "f16", True, False),     # one token: one output tile, K split 2 ways, compensator 4
     (96, 1024, 0, 16, 16, "bf16", False, True),    # 16 tokens, per-channel, concurrent schedule
+    (1, 32, 0, 2, 40, "bf16", False, False),       # one output row, the smallest K
     (160, 256, 128, 32, 300, "bf16", True, False), # K < 512: one compensator split forms U itself
     (200, 512, 128, 100, 77, "f16", False, True),  # rank 100: padded U rows, 7 row blocks of [A; w_g]
     (256, 4096, 128, 32, 100, "f16", True, False),  # 2 output tiles: K split 8 ways, serial
