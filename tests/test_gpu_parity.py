@@ -124,6 +124,8 @@ DECODE_CASES = [
     (48, 8192, 0, 4, 2, "bf16", False),      # long K, several staged chunks at M = 2
     (33, 96, 0, 1, 1, "f16", False),         # rank 1, tiny K
     (1, 32, 0, 2, 2, "f16", False),          # one output row, the smallest K (one 32-wide piece)
+    (160, 1024, 128, 128, 32, "f16", True),  # the largest rank (9 row blocks of [A; w_g]), 2 token blocks
+    (64, 512, 0, 128, 1, "bf16", False),     # the largest rank at one token
 ]
 
 
@@ -201,6 +203,8 @@ RANK_GATE_CASES = [
     ("decode", 200, 1024, 128, 32, 16, 1, "f16", 0.7),
     ("decode", 136, 2048, 0, 24, 8, 5, "bf16", 1.3),
     ("decode", 96, 512, 128, 40, 64, 32, "f16", 1.0),
+    ("decode", 96, 512, 128, 128, 64, 32, "f16", 1.0),     # the largest rank and hidden width
+    ("prefill", 96, 512, 128, 128, 64, 70, "bf16", 1.0),
     ("prefill", 264, 1024, 128, 32, 16, 70, "f16", 0.7),
     ("prefill", 128, 4096, 128, 16, 32, 40, "bf16", 0.5),   # K split, many compensator splits
     ("prefill_aux", 200, 1024, 0, 32, 16, 150, "f16", 1.0),
@@ -387,6 +391,8 @@ PREFILL_CASES = [
     (96, 1024, 128, 8, 1, "f16", True, False),     # one token: one output tile, K split 2 ways, compensator 4
     (96, 1024, 0, 16, 16, "bf16", False, True),    # 16 tokens, per-channel, concurrent schedule
     (1, 32, 0, 2, 40, "bf16", False, False),       # one output row, the smallest K
+    (256, 1024, 128, 128, 150, "f16", True, False),  # the largest rank, serial: 4 epilogue rank chunks
+    (256, 1024, 128, 128, 150, "bf16", True, True),  # the largest rank, concurrent schedule
     (160, 256, 128, 32, 300, "bf16", True, False), # K < 512: one compensator split forms U itself
     (200, 512, 128, 100, 77, "f16", False, True),  # rank 100: padded U rows, 7 row blocks of [A; w_g]
     (256, 4096, 128, 32, 100, "f16", True, False),  # 2 output tiles: K split 8 ways, serial
