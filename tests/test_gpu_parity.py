@@ -126,6 +126,7 @@ DECODE_CASES = [
     (1, 32, 0, 2, 2, "f16", False),          # one output row, the smallest K (one 32-wide piece)
     (160, 1024, 128, 128, 32, "f16", True),  # the largest rank (9 row blocks of [A; w_g]), 2 token blocks
     (64, 512, 0, 128, 1, "bf16", False),     # the largest rank at one token
+    (48, 20480, 0, 8, 4, "f16", True),       # K past 16384: producer splits capped, two passes per wave
 ]
 
 
