@@ -141,9 +141,9 @@ typedef struct spear_layer {
  *
  * Compensated layers need a workspace for every call.  For a layer with
  * r == 0 it is optional: prefill uses it to split K across workgroups when
- * the output has few 128 x 128 tiles (small M), and decode with
- * M >= spear_get_decode_split_min_m() uses it to split K across the
- * workgroups of each 128-row output tile.  Decode takes that split launch
+ * the output has few 128 x 128 tiles (small M), and decode uses it to
+ * split K across the workgroups of each 128-row output tile where the
+ * thresholds of spear_set_decode_split_min_m and _min_k ask for that.  Decode takes that split launch
  * only when the workspace given is at least this size for the call's M;
  * with a smaller (or no) workspace it runs the unsplit launch.
  */
@@ -163,8 +163,8 @@ spear_status_t spear_pack_int4(const uint8_t *q, int32_t *qweight, int64_t N, in
  * x [M][K] and y [M][N] are row-major activation-type device arrays, x and y
  * 16-byte aligned.  The gate, A x and the gated B (A x) term are computed in
  * the same launch as the 4-bit product and added before y is rounded.
- * M == 0 is a no-op.  From spear_get_decode_split_min_m() tokens on, and when
- * K >= spear_get_decode_split_min_k() and the workspace has
+ * M == 0 is a no-op.  Where the split thresholds ask for it (see
+ * spear_set_decode_split_min_m) and the workspace has
  * spear_workspace_bytes(layer, M) bytes, the launch splits
  * K across the workgroups of each 128-row output tile (the last split to
  * finish a tile sums the tile's partials in split order and applies the
@@ -203,10 +203,13 @@ spear_status_t spear_set_decode_max_m(int32_t m);
 int32_t spear_get_decode_max_m(void);
 
 /*
- * When decode considers the split-K launch: from M = spear_get_decode_split_min_m()
- * tokens on, 1..SPEAR_MAX_DECODE_M + 1 (default 16; SPEAR_MAX_DECODE_M + 1 switches
- * it off), for layers with K >= spear_get_decode_split_min_k() (>= 1, default
- * 8192).  Process-wide.  Set them before sizing workspaces: spear_workspace_bytes
+ * When decode considers the split-K launch: for layers with
+ * K >= spear_get_decode_split_min_k() (>= 1, default 8192), from
+ * M = spear_get_decode_split_min_m() tokens on (1..SPEAR_MAX_DECODE_M + 1,
+ * default 16; SPEAR_MAX_DECODE_M + 1 switches the split off), and, for layers
+ * with K at least twice the column threshold, from a quarter of the token
+ * threshold on (4 * M >= min_m; with the defaults, M >= 4 from K = 16384).
+ * Process-wide.  Set them before sizing workspaces: spear_workspace_bytes
  * includes the split launch's partial tiles only for the calls it applies to.
  */
 spear_status_t spear_set_decode_split_min_m(int32_t m);

@@ -84,6 +84,7 @@ struct DecodePlan {
 bool decode_supported(const LayerDesc &L, int M);
 size_t decode_workspace_bytes(const LayerDesc &L, int M);       // required
 size_t decode_fast_workspace_bytes(const LayerDesc &L, int M);  // enough for the split-K launch
+bool decode_split_wanted(int M, int K);  // the token and column thresholds (decode.hip)
 void set_decode_split_min_m(int m);
 int get_decode_split_min_m();
 void set_decode_split_min_k(int k);

@@ -342,20 +342,40 @@ def test_decode_workspace_reuse_many_calls():
 
 def test_decode_split_needs_room_in_the_workspace():
     """K >= 8192 at 16 tokens takes the split-K launch when the workspace holds its
-    partial tiles, and the unsplit launch with a workspace sized for one token; both
+    partial tiles, and the unsplit launch when it holds only what that needs; both
     match the oracle."""
     note("decode split-K fallback on a small workspace")
     hl, xb, lay, x = _setup(256, 8192, 128, 32, seed=61, M=16, outliers=True)
     ref = oracle_y(hl, xb)
     big = spear.new_workspace(lay, 16)
-    small = spear.new_workspace(lay, 1)
-    assert small.numel() < big.numel()
+    # the unsplit launch needs the header and the producers' partials: 3 row blocks
+    # of [A; w_g] x 4 K-splits x 16 rows x 16 tokens x 4 bytes = 12288 bytes; the
+    # split launch adds 2 tiles x 8 K-splits x 8 waves x 64 lanes x 16 bytes = 131072
+    small = big[: WS_HEADER_BYTES + 12288 + 65536]
     y_split = spear.spear_linear_decode(lay, x, workspace=big)
+    torch.cuda.synchronize()
     y_plain = spear.spear_linear_decode(lay, x, workspace=small)
     torch.cuda.synchronize()
     assert_close(gpu_y_f64(y_split, "f16"), ref, "split")
     assert_close(gpu_y_f64(y_plain, "f16"), ref, "unsplit")
-    assert _ws_header(big) == [0] * 12 and _ws_header(small) == [0] * 12
+    assert _ws_header(big) == [0] * 12
+    with pytest.raises(spear.SpearError):  # below what the unsplit launch needs
+        spear.spear_linear_decode(lay, x, workspace=big[: WS_HEADER_BYTES + 4096])
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_decode_long_k_default_thresholds(M):
+    """K = 20480 >= twice the column threshold: the default thresholds take the split-K
+    launch from 4 tokens on and the one-launch kernel below; both match the oracle."""
+    note(f"decode long K default thresholds M={M}")
+    assert spear.spear_get_decode_split_min_m() == 16
+    assert spear.spear_get_decode_split_min_k() == 8192
+    hl, xb, lay, x = _setup(384, 20480, 0, 24, seed=71 + M, M=M, outliers=True)
+    ws = spear.new_workspace(lay, M)
+    y = spear.spear_linear_decode(lay, x, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(gpu_y_f64(y, "f16"), oracle_y(hl, xb), f"long K M={M}")
+    assert _ws_header(ws) == [0] * 12
 
 
 def test_decode_fresh_inputs_every_call():
