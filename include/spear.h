@@ -207,8 +207,8 @@ int32_t spear_get_decode_max_m(void);
  * K >= spear_get_decode_split_min_k() (>= 1, default 8192), from
  * M = spear_get_decode_split_min_m() tokens on (1..SPEAR_MAX_DECODE_M + 1,
  * default 16; SPEAR_MAX_DECODE_M + 1 switches the split off), and, for layers
- * with K at least twice the column threshold, from a quarter of the token
- * threshold on (4 * M >= min_m; with the defaults, M >= 4 from K = 16384).
+ * with K at least twice the column threshold, from an eighth of the token
+ * threshold on (8 * M >= min_m; with the defaults, M >= 2 from K = 16384).
  * Process-wide.  Set them before sizing workspaces: spear_workspace_bytes
  * includes the split launch's partial tiles only for the calls it applies to.
  */

@@ -31,13 +31,14 @@ std::atomic<int> g_split_min_k{8192};
 
 // Split-K wanted for M tokens at K columns (its plan must still fit and the
 // workspace hold its partial tiles): from the token threshold on, and, where
-// K is at least twice the column threshold, from a quarter of it on (at
-// 28672 -> 8192 with M = 4 the split call takes 44.8 us against 54.7; at
-// M = 1 it loses).  A token threshold past 32 turns the split off.
+// K is at least twice the column threshold, from an eighth of it on (at
+// 28672 -> 8192 the split call takes 43.9 / 44.0 / 44.4 us at M = 2 / 3 / 4
+// against 49.0 / 54.2 / 54.7 unsplit; at M = 1 it loses, 43.4 against
+// 34.2).  A token threshold past 32 turns the split off.
 bool decode_split_wanted(int M, int K) {
   const int mm = g_split_min_m.load(), mk = g_split_min_k.load();
   if (mm > 32 || K < mk) return false;
-  return M >= mm || ((long long)K >= 2LL * mk && 4 * M >= mm);
+  return M >= mm || ((long long)K >= 2LL * mk && 8 * M >= mm);
 }
 
 void set_decode_split_min_m(int m) { g_split_min_m.store(m); }
