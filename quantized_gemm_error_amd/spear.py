@@ -202,23 +202,101 @@ def new_workspace(layer: SpearLayer, M: int, device="cuda"):
 def spear_pack_int4(q, qweight=None, stream=None):
     """uint8 codes [N][K] (device) -> int32 packed words [N][K/8] (device)."""
     import torch
+    _require(q.dim() == 2 and q.dtype == torch.uint8, "q must be a 2-D uint8 tensor [N][K]",
+             TypeError)
+    _require(q.is_contiguous(), "q must be contiguous")
     N, K = q.shape
+    _require(K % 8 == 0, f"K={K} is not a multiple of 8")
     if qweight is None:
         qweight = torch.empty((N, K // 8), dtype=torch.int32, device=q.device)
+    _check_tensor(qweight, "qweight", (N, K // 8), (torch.int32,))
+    _require(q.device.type == "cuda" and qweight.device == q.device,
+             f"q and qweight must be on one GPU (got {q.device} and {qweight.device})")
     _check(load_library().spear_pack_int4(_ptr(q), _ptr(qweight), N, K, _stream(stream)))
     return qweight
 
 
-def _io(layer, x, y):
+def _require(cond, msg: str, exc=ValueError) -> None:
+    if not cond:
+        raise exc(msg)
+
+
+def _check_tensor(t, name: str, shape, dtypes) -> None:
+    """t is a contiguous tensor of exactly `shape` with a dtype in `dtypes`."""
+    _require(t is not None, f"{name} is missing")
+    _require(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _require(t.dtype in dtypes, f"{name} has dtype {t.dtype}, expected one of {dtypes}", TypeError)
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _check_layer(layer: "SpearLayer", act) -> None:
+    """Shapes, dtypes and contiguity of the layer's tensors, with activations of dtype act.
+
+    The C ABI receives bare pointers and cannot check any of this; a wrong shape or
+    stride would make the kernels read past the end of a buffer."""
     import torch
+    N, K, G, r = layer.N, layer.K, layer.group_size, layer.rank
+    _require(N >= 1 and K >= 1 and G >= 1 and K % G == 0 and K % 8 == 0,
+             f"invalid layer geometry N={N} K={K} group_size={G}")
+    bits16 = (torch.float16, torch.int16)   # fp16 values or their bit patterns
+    _check_tensor(layer.qweight, "qweight", (N, K // 8), (torch.int32,))
+    _check_tensor(layer.scales, "scales", (N, K // G), bits16)
+    _check_tensor(layer.zeros, "zeros", (N, K // G), bits16)
+    if r > 0:
+        _check_tensor(layer.A, "A", (r, K), (act,))
+        _check_tensor(layer.B, "B", (N, r), (act,))
+        if layer.rank_gate is None:
+            _check_tensor(layer.w_gate, "w_gate", (K,), (act,))
+        else:
+            g = layer.rank_gate
+            h = int(g.hidden)
+            f32 = (torch.float32,)
+            _check_tensor(g.W1, "rank_gate.W1", (h, r), f32)
+            _check_tensor(g.b1, "rank_gate.b1", (h,), f32)
+            _check_tensor(g.W2, "rank_gate.W2", (r, h), f32)
+            _check_tensor(g.b2, "rank_gate.b2", (r,), f32)
+
+
+def _layer_tensors(layer: "SpearLayer"):
+    ts = [layer.qweight, layer.scales, layer.zeros]
+    if layer.rank > 0:
+        ts += [layer.A, layer.B, layer.w_gate]
+        if layer.rank_gate is not None:
+            g = layer.rank_gate
+            ts += [g.W1, g.b1, g.W2, g.b2]
+    return [t for t in ts if t is not None]
+
+
+def _io(layer, x, y, workspace=None):
+    """Check x, y, the workspace and the layer against each other; allocate y if None."""
+    import torch
+    _dtype_code(x)
+    _require(x.dim() == 2, f"x must be 2-D [M][K], got {x.dim()}-D")
+    _require(x.shape[1] == layer.K, f"x has {x.shape[1]} columns, the layer has K={layer.K}")
+    _require(x.is_contiguous(), "x must be contiguous (row-major [M][K])")
+    _check_layer(layer, x.dtype)
     M = x.shape[0]
+    if y is not None:
+        _check_tensor(y, "y", (M, layer.N), (x.dtype,))
+    if workspace is not None:
+        _require(workspace.is_contiguous(), "workspace must be contiguous")
+    dev = x.device
+    _require(dev.type == "cuda", f"x must be a GPU tensor, got {dev}")
+    others = _layer_tensors(layer) + ([y] if y is not None else []) + \
+        ([workspace] if workspace is not None else [])
+    for t in others:
+        _require(t.device == dev, f"every tensor must be on {dev}; found one on {t.device}")
     if y is None:
-        y = torch.empty((M, layer.N), dtype=x.dtype, device=x.device)
+        y = torch.empty((M, layer.N), dtype=x.dtype, device=dev)
+    else:
+        xs, xe = x.data_ptr(), x.data_ptr() + x.numel() * x.element_size()
+        ys, ye = y.data_ptr(), y.data_ptr() + y.numel() * y.element_size()
+        _require(ye <= xs or xe <= ys or x.numel() == 0 or y.numel() == 0, "y must not overlap x")
     return M, y
 
 
 def spear_linear_decode(layer: SpearLayer, x, y=None, workspace=None, stream=None):
-    M, y = _io(layer, x, y)
+    M, y = _io(layer, x, y, workspace)
     c = layer.as_c()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().spear_linear_decode(ctypes.byref(c), _dtype_code(x), _ptr(x), _ptr(y), M,
@@ -228,7 +306,7 @@ def spear_linear_decode(layer: SpearLayer, x, y=None, workspace=None, stream=Non
 
 def spear_linear_prefill(layer: SpearLayer, x, y=None, workspace=None, main_stream=None,
                          aux_stream=None):
-    M, y = _io(layer, x, y)
+    M, y = _io(layer, x, y, workspace)
     c = layer.as_c()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     aux = None if aux_stream is None else _stream(aux_stream)
@@ -238,7 +316,7 @@ def spear_linear_prefill(layer: SpearLayer, x, y=None, workspace=None, main_stre
 
 
 def spear_linear(layer: SpearLayer, x, y=None, workspace=None, main_stream=None, aux_stream=None):
-    M, y = _io(layer, x, y)
+    M, y = _io(layer, x, y, workspace)
     c = layer.as_c()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     aux = None if aux_stream is None else _stream(aux_stream)
