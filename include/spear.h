@@ -208,7 +208,8 @@ int32_t spear_get_decode_max_m(void);
  * M = spear_get_decode_split_min_m() tokens on (1..SPEAR_MAX_DECODE_M + 1,
  * default 16; SPEAR_MAX_DECODE_M + 1 switches the split off), and, for layers
  * with K at least twice the column threshold, from an eighth of the token
- * threshold on (8 * M >= min_m; with the defaults, M >= 2 from K = 16384).
+ * threshold on but never below 2 tokens (M >= max(2, ceil(min_m / 8)); with
+ * the defaults, M >= 2 from K = 16384).
  * Process-wide.  Set them before sizing workspaces: spear_workspace_bytes
  * includes the split launch's partial tiles only for the calls it applies to.
  */
@@ -226,6 +227,37 @@ int32_t spear_get_decode_split_min_k(void);
  */
 int32_t spear_select_chunk(const int32_t *chunks, const float *pred_ms, int32_t n,
                            float budget_ms, int32_t *violated);
+
+/*
+ * Which launch a call takes, computed on the host without launching anything
+ * (the same planning that spear_linear, spear_linear_decode and
+ * spear_linear_prefill run).  For inspection and tests; the compute calls do
+ * not need it.
+ */
+typedef enum spear_path {
+  SPEAR_PATH_NONE = 0,          /* M == 0: nothing is launched */
+  SPEAR_PATH_DECODE = 1,        /* fused decode, one workgroup per group of output rows */
+  SPEAR_PATH_DECODE_SPLIT = 2,  /* fused decode, K split across each 128-row tile's workgroups */
+  SPEAR_PATH_PREFILL = 3        /* the prefill GEMM path */
+} spear_path_t;
+
+typedef struct spear_plan {
+  int32_t path;                /* a spear_path_t */
+  int32_t workgroups;          /* of the main launch (decode: producers included) */
+  int32_t waves_per_workgroup; /* of the main launch */
+  int32_t producers;           /* decode: compensator workgroups of the launch (0 at rank 0) */
+  int32_t k_splits;            /* splits of K in the main product (1: none) */
+  size_t workspace_bytes;      /* the least workspace this call accepts (0: none needed) */
+} spear_plan_t;
+
+/*
+ * Plan of spear_linear (phase = 0), spear_linear_decode (1) or
+ * spear_linear_prefill (2) for this layer, M tokens and a workspace of
+ * workspace_bytes (0: no workspace) into *plan (host memory).  Returns the
+ * status the call itself would return for a valid x and y.
+ */
+spear_status_t spear_linear_plan(const spear_layer_t *layer, int32_t M, size_t workspace_bytes,
+                                 int32_t phase, spear_plan_t *plan);
 
 /* Static description of a status code. */
 const char *spear_status_string(spear_status_t status);

@@ -200,6 +200,37 @@ spear_status_t spear_linear(const spear_layer_t *layer, spear_dtype_t dtype, con
                               aux_stream);
 }
 
+spear_status_t spear_linear_plan(const spear_layer_t *layer, int32_t M, size_t workspace_bytes,
+                                 int32_t phase, spear_plan_t *plan) {
+  if (!plan) return fail(SPEAR_ERR_INVALID_ARGUMENT, "plan must not be NULL");
+  if (phase < 0 || phase > 2)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "phase=%d: 0 (dispatch), 1 (decode) or 2 (prefill)", phase);
+  *plan = spear_plan_t{};
+  LayerDesc d;
+  spear_status_t st = check_layer(layer, &d);
+  if (st != SPEAR_OK) return st;
+  const bool decode = phase == 1 || (phase == 0 && M >= 0 && M <= g_decode_max_m.load());
+  if (decode && (M < 0 || M > SPEAR_MAX_DECODE_M))
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode M=%d outside 0..%d", M, SPEAR_MAX_DECODE_M);
+  if (!decode && M < 0) return fail(SPEAR_ERR_INVALID_ARGUMENT, "prefill M=%d must be >= 0", M);
+  if (!decode && M > (1 << 24)) return fail(SPEAR_ERR_UNSUPPORTED, "prefill M=%d too large", M);
+  if (M == 0) return ok();
+  // the workspace checks of the calls, with any non-null 256-byte aligned pointer
+  void *const ws = workspace_bytes > 0 ? (void *)(uintptr_t)256 : nullptr;
+  if (decode) {
+    if (!decode_supported(d, M))
+      return fail(SPEAR_ERR_UNSUPPORTED, "no decode launch shape fits K=%d G=%d M=%d", d.K, d.G, M);
+    if ((st = check_ws(ws, workspace_bytes, decode_workspace_bytes(d, M))) != SPEAR_OK) return st;
+    describe_decode(d, M, workspace_bytes, plan);
+  } else {
+    if ((ws || prefill_needs_workspace(d)) &&
+        (st = check_ws(ws, workspace_bytes, prefill_workspace_bytes(d, M))) != SPEAR_OK)
+      return st;
+    describe_prefill(d, M, workspace_bytes, plan);
+  }
+  return ok();
+}
+
 spear_status_t spear_set_decode_max_m(int32_t m) {
   if (m < 1 || m > SPEAR_MAX_DECODE_M)
     return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode_max_m=%d outside 1..%d", m, SPEAR_MAX_DECODE_M);

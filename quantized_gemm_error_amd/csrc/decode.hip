@@ -31,14 +31,15 @@ std::atomic<int> g_split_min_k{8192};
 
 // Split-K wanted for M tokens at K columns (its plan must still fit and the
 // workspace hold its partial tiles): from the token threshold on, and, where
-// K is at least twice the column threshold, from an eighth of it on (at
-// 28672 -> 8192 the split call takes 43.9 / 44.0 / 44.4 us at M = 2 / 3 / 4
-// against 49.0 / 54.2 / 54.7 unsplit; at M = 1 it loses, 43.4 against
-// 34.2).  A token threshold past 32 turns the split off.
+// K is at least twice the column threshold, from an eighth of it on, but
+// never below 2 tokens (at 28672 -> 8192 the split call takes 43.9 / 44.0 /
+// 44.4 us at M = 2 / 3 / 4 against 49.0 / 54.2 / 54.7 unsplit; at M = 1 it
+// loses, 43.4 against 34.2).  A token threshold past 32 turns the split off.
 bool decode_split_wanted(int M, int K) {
   const int mm = g_split_min_m.load(), mk = g_split_min_k.load();
   if (mm > 32 || K < mk) return false;
-  return M >= mm || ((long long)K >= 2LL * mk && 8 * M >= mm);
+  const int long_k_min = (mm + 7) / 8 < 2 ? 2 : (mm + 7) / 8;
+  return M >= mm || ((long long)K >= 2LL * mk && M >= long_k_min);
 }
 
 void set_decode_split_min_m(int m) { g_split_min_m.store(m); }
@@ -57,6 +58,11 @@ size_t decode_workspace_bytes(const LayerDesc &L, int M) {
 size_t decode_fast_workspace_bytes(const LayerDesc &L, int M) {
   return four_waves(L, M) ? w4::decode_fast_workspace_bytes(L, M)
                           : w8::decode_fast_workspace_bytes(L, M);
+}
+
+void describe_decode(const LayerDesc &L, int M, size_t ws_bytes, spear_plan_t *out) {
+  four_waves(L, M) ? w4::describe_decode(L, M, ws_bytes, out)
+                   : w8::describe_decode(L, M, ws_bytes, out);
 }
 
 hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,

@@ -97,10 +97,13 @@ int get_decode_split_min_k();
   size_t decode_workspace_bytes(const LayerDesc &L, int M);                               \
   size_t decode_fast_workspace_bytes(const LayerDesc &L, int M);                          \
   hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, \
-                           int M, void *ws, size_t ws_bytes, hipStream_t s);
+                           int M, void *ws, size_t ws_bytes, hipStream_t s);               \
+  void describe_decode(const LayerDesc &L, int M, size_t ws_bytes, spear_plan_t *out);
 namespace w8 { SPEAR_DECODE_VARIANT_API }
 namespace w4 { SPEAR_DECODE_VARIANT_API }
 #undef SPEAR_DECODE_VARIANT_API
+void describe_decode(const LayerDesc &L, int M, size_t ws_bytes, spear_plan_t *out);
+void describe_prefill(const LayerDesc &L, int M, size_t ws_bytes, spear_plan_t *out);
 size_t prefill_workspace_bytes(const LayerDesc &L, int M);
 bool prefill_needs_workspace(const LayerDesc &L);  // false: optional (splits K when given)
 

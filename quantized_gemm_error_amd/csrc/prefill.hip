@@ -34,6 +34,7 @@
 //  * concurrent (aux stream given, the pages' schedule): the compensator on
 //    the aux stream alongside the GEMM on the main stream; after the join the
 //    finish kernel adds U B^T.
+#include <algorithm>
 #include <mutex>
 #include <unordered_map>
 
@@ -906,12 +907,34 @@ static int prefill_tail_rows(int M, int N, int K) {
   return gemm_ksplit(tail, N, K) > 1 ? tail : 0;
 }
 
-// Workspace layout after the 2048-byte header: the compensator's split
-// partials [ks][M][rp1], U [M][rp1] formed from them, and the GEMM's
-// split partials (at most kGemmSplitWgs tiles of 128 x 128 fp32).  All are
-// rewritten in full by every call before they are read and are sized by
-// bounds that grow with M, so a workspace for M serves every call with fewer
-// tokens, and any other layer whose size it covers.
+// Bytes of the GEMM's split partials [ks][m][N] fp32 that any call with 1..M
+// tokens stores: a K-split GEMM over all m rows, or over the ragged tail's
+// rows.  ks depends on m only through its tile rows, so ks m peaks at the
+// last m of each band of 128 rows; both loops stop where no split happens
+// (the output fills the chip, or the tail exceeds a quarter of the CUs).
+static size_t gemm_partial_bytes(int M, int N, int K) {
+  const int ntn = (N + BN - 1) / BN;
+  size_t most = 0;
+  for (int tr = 1; (tr - 1) * BM < M && tr * ntn < kGemmSplitWgs * 3 / 4; ++tr) {
+    const int m = std::min(M, tr * BM);
+    const int ks = gemm_ksplit(m, N, K);
+    if (ks > 1) most = std::max(most, (size_t)ks * m * N * sizeof(float));
+  }
+  for (int tr = 1; (tr - 1) * BM < M && tr * ntn * 4 <= kGemmCus; ++tr) {
+    const int t = std::min(M, tr * BM);  // tail rows of at most tr tile rows
+    const int ks = gemm_ksplit(t, N, K);
+    if (ks > 1) most = std::max(most, (size_t)ks * t * N * sizeof(float));
+  }
+  return most;
+}
+
+// Workspace layout after the header: the compensator's split partials
+// [ks][M][rp1], U [M][rp1] formed from them, and the GEMM's split partials
+// (at most kGemmSplitWgs tiles of 128 x 128 fp32, and only as many as a call
+// with at most M tokens can split into).  All are rewritten in full by every
+// call before they are read and are sized by bounds that grow with M, so a
+// workspace for M serves every call with fewer tokens, and any other layer
+// whose size it covers.
 struct PrefillWs {
   size_t tp, ts, gpart, end;
 };
@@ -924,13 +947,25 @@ static PrefillWs prefill_ws_layout(const LayerDesc &L, int M) {
   const size_t sb = L.rank > 0 ? round256((size_t)M * rp1 * sizeof(float)) : 0;
   w.ts = w.tp + tb;
   w.gpart = w.ts + sb;
-  w.end = w.gpart + (size_t)kGemmSplitWgs * BM * BN * sizeof(float);
+  w.end = w.gpart + round256(gemm_partial_bytes(M, L.N, L.K));
   return w;
 }
 
 size_t prefill_workspace_bytes(const LayerDesc &L, int M) { return prefill_ws_layout(L, M).end; }
 
 bool prefill_needs_workspace(const LayerDesc &L) { return L.rank > 0; }
+
+void describe_prefill(const LayerDesc &L, int M, size_t ws_bytes, spear_plan_t *out) {
+  const int gks = ws_bytes > 0 ? gemm_ksplit(M, L.N, L.K) : 1;
+  const int tail = (ws_bytes > 0 && gks == 1) ? prefill_tail_rows(M, L.N, L.K) : 0;
+  const int ntn = (L.N + BN - 1) / BN;
+  out->path = SPEAR_PATH_PREFILL;
+  out->workgroups = ntn * ((M - tail + BM - 1) / BM) * gks;
+  out->waves_per_workgroup = 4;
+  out->producers = 0;
+  out->k_splits = gks;
+  out->workspace_bytes = prefill_needs_workspace(L) ? prefill_workspace_bytes(L, M) : 0;
+}
 
 template <int DT, bool PERCH>
 static void launch_gemm(const GemmArgs &g, dim3 grid, bool epi, hipStream_t s) {

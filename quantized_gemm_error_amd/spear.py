@@ -32,7 +32,14 @@ EXPORTED = (
     "spear_set_decode_split_min_m", "spear_get_decode_split_min_m",
     "spear_set_decode_split_min_k", "spear_get_decode_split_min_k", "spear_select_chunk",
     "spear_status_string", "spear_last_error", "spear_workspace_flags", "spear_version",
+    "spear_linear_plan",
 )
+
+SPEAR_PATH_NONE = 0
+SPEAR_PATH_DECODE = 1
+SPEAR_PATH_DECODE_SPLIT = 2
+SPEAR_PATH_PREFILL = 3
+PATH_NAMES = {0: "none", 1: "decode", 2: "decode_split", 3: "prefill"}
 
 
 class SpearError(RuntimeError):
@@ -57,6 +64,14 @@ class SpearLayerC(ctypes.Structure):
         ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
         ("b_gate", ctypes.c_float),
         ("rank_gate", ctypes.POINTER(SpearRankGateC)),
+    ]
+
+
+class SpearPlanC(ctypes.Structure):
+    _fields_ = [
+        ("path", ctypes.c_int32), ("workgroups", ctypes.c_int32),
+        ("waves_per_workgroup", ctypes.c_int32), ("producers", ctypes.c_int32),
+        ("k_splits", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -107,6 +122,8 @@ def load_library(path: str = LIB_PATH):
     lib.spear_workspace_flags.restype = i32
     lib.spear_version.argtypes = []
     lib.spear_version.restype = i32
+    lib.spear_linear_plan.argtypes = [LP, i32, sz, i32, ctypes.POINTER(SpearPlanC)]
+    lib.spear_linear_plan.restype = i32
     _lib = lib
     return lib
 
@@ -376,6 +393,19 @@ def spear_workspace_flags(workspace, stream=None) -> int:
     flags = ctypes.c_uint32(0)
     _check(load_library().spear_workspace_flags(_ptr(workspace), ctypes.byref(flags), _stream(stream)))
     return int(flags.value)
+
+
+def spear_linear_plan(layer, M: int, workspace_bytes: int = 0, phase: str = "dispatch") -> dict:
+    """The launch a call would take (nothing is launched): phase "dispatch" (spear_linear),
+    "decode" or "prefill".  `layer` is a SpearLayer or a SpearLayerC."""
+    c = layer if isinstance(layer, SpearLayerC) else layer.as_c()
+    code = {"dispatch": 0, "decode": 1, "prefill": 2}[phase]
+    out = SpearPlanC()
+    _check(load_library().spear_linear_plan(ctypes.byref(c), int(M), int(workspace_bytes), code,
+                                            ctypes.byref(out)))
+    return {"path": PATH_NAMES.get(out.path, str(out.path)), "workgroups": out.workgroups,
+            "waves_per_workgroup": out.waves_per_workgroup, "producers": out.producers,
+            "k_splits": out.k_splits, "workspace_bytes": int(out.workspace_bytes)}
 
 
 def spear_version() -> int:

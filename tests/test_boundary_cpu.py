@@ -191,3 +191,84 @@ def test_workspace_bytes(lib):
     assert small >= 256 and big >= 2048 * 8 * 4
     assert lib.spear_workspace_bytes(ctypes.byref(_layer(K=250)), 1) == 0
     assert lib.spear_workspace_bytes(ctypes.byref(lay), -1) == 0
+
+
+def _plan(layer, M, ws_bytes, phase="dispatch"):
+    return spear.spear_linear_plan(layer, M, ws_bytes, phase)
+
+
+@pytest.mark.parametrize("K", [4096, 8192, 16384, 28672])
+@pytest.mark.parametrize("min_m", [1, 2, 4, 8, 9, 16, 33])
+def test_decode_split_truth_table(lib, K, min_m):
+    """Which token counts may take the split-K decode launch: M >= min_m at K >= min_k,
+    and M >= max(2, ceil(min_m / 8)) at K >= 2 min_k; never with min_m = 33 and never
+    without room for the partial tiles.  (A wanted split still needs its plan to fit,
+    every workgroup resident at once; the cases that fit are checked below.)"""
+    lay = _layer(N=8192, K=K, group_size=K, rank=64)
+    old = spear.spear_get_decode_split_min_m(), spear.spear_get_decode_split_min_k()
+    spear.spear_set_decode_split_min_m(min_m)
+    spear.spear_set_decode_split_min_k(8192)
+    try:
+        big = lib.spear_workspace_bytes(ctypes.byref(lay), 32)
+        for M in range(1, 33):
+            want = min_m <= 32 and K >= 8192 and (
+                M >= min_m or (K >= 16384 and M >= max(2, -(-min_m // 8))))
+            p = _plan(lay, M, big)
+            if not want:
+                assert p["path"] == "decode", (M, p)
+            if p["path"] == "decode_split":
+                assert p["k_splits"] >= 2
+                # with only the unsplit launch's workspace, the same call does not split
+                assert _plan(lay, M, p["workspace_bytes"])["path"] == "decode"
+    finally:
+        spear.spear_set_decode_split_min_m(old[0])
+        spear.spear_set_decode_split_min_k(old[1])
+
+
+@pytest.mark.parametrize("K,N,G,r,M", [(28672, 8192, 28672, 64, m) for m in range(2, 9)] +
+                         [(11008, 4096, 128, 32, 16), (11008, 4096, 128, 32, 32),
+                          (20480, 384, 20480, 24, 2)])
+def test_decode_split_taken_with_default_thresholds(lib, K, N, G, r, M):
+    """The Llama-70B 28672->8192 layer (per-channel, rank 64) and the Llama-7B 11008->4096
+    layer (g128, rank 32) take the split-K launch where it was measured to win."""
+    assert spear.spear_get_decode_split_min_m() == 16
+    assert spear.spear_get_decode_split_min_k() == 8192
+    lay = _layer(N=N, K=K, group_size=G, rank=r)
+    ws = lib.spear_workspace_bytes(ctypes.byref(lay), 32)
+    assert _plan(lay, M, ws)["path"] == "decode_split"
+    assert _plan(lay, 1, ws)["path"] == "decode"        # one token never splits by default
+
+
+def test_plan_dispatch_and_errors(lib):
+    lay = _layer(N=4096, K=4096, group_size=128, rank=32)
+    ws = lib.spear_workspace_bytes(ctypes.byref(lay), 2048)
+    assert _plan(lay, 0, ws)["path"] == "none"
+    assert _plan(lay, 1, ws)["path"] == "decode"
+    assert _plan(lay, 32, ws)["path"] == "decode"
+    assert _plan(lay, 33, ws)["path"] == "prefill"
+    assert _plan(lay, 2048, ws)["path"] == "prefill"
+    assert _plan(lay, 2048, ws)["k_splits"] == 1
+    assert _plan(lay, 64, ws)["k_splits"] > 1          # 32 output tiles: K split
+    assert _plan(lay, 16, ws, "prefill")["path"] == "prefill"
+    with pytest.raises(spear.SpearError):
+        _plan(lay, 33, ws, "decode")
+    with pytest.raises(spear.SpearError):               # compensated: workspace required
+        _plan(lay, 1, 0)
+    with pytest.raises(spear.SpearError):
+        _plan(lay, 2048, 1024)
+    lay0 = _layer(N=4096, K=4096, group_size=128, rank=0, A=None, B=None, w_gate=None)
+    assert _plan(lay0, 100, 0)["k_splits"] == 1        # rank 0 without a workspace: no split
+    assert _plan(lay0, 100, 0)["workspace_bytes"] == 0
+
+
+def test_workspace_holds_only_the_partials_a_call_can_split_into(lib):
+    """Decode-sized workspaces carry no 32 MiB of GEMM partials: at M <= 32 the prefill
+    split partials are at most ks * 32 * N * 4 bytes."""
+    lay = _layer(N=4096, K=4096, group_size=128, rank=32)
+    small = lib.spear_workspace_bytes(ctypes.byref(lay), 32)
+    assert small <= 16 * 32 * 4096 * 4 + (2 << 20), small
+    assert small < lib.spear_workspace_bytes(ctypes.byref(lay), 2048)
+    for M in (1, 16, 32, 33, 64, 200, 640, 2048):
+        need = lib.spear_workspace_bytes(ctypes.byref(lay), M)
+        plan = _plan(lay, M, need)
+        assert plan["workspace_bytes"] <= need
