@@ -45,6 +45,23 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# Sticky error words of the workspaces each leg used (bit 0: a decode launch gave up
+# waiting for its compensator producers).  Recorded in the JSON line; any bit set makes
+# the run exit with status 3 after printing it.
+WS_FLAGS: dict = {}
+
+
+def record_flags(leg: str, workspaces) -> None:
+    from quantized_gemm_error_amd import spear
+    word = 0
+    for ws in workspaces:
+        if ws is not None:
+            word |= spear.spear_workspace_flags(ws)
+    WS_FLAGS[leg] = WS_FLAGS.get(leg, 0) | word
+    if word:
+        log(f"workspace flags {word:#x} after {leg}")
+
+
 # ---------------------------------------------------------------------------
 # algorithmic work of one call (bytes the method must move, flops it must do)
 # ---------------------------------------------------------------------------
@@ -320,6 +337,7 @@ def prefill_context(torch, device):
         def run_r0(_i, s):
             spear.spear_linear_prefill(lay0, x, y=y, workspace=ws, main_stream=s)
         t = graph_times_ms(torch, {"serial": run_serial, "conc": run_conc, "r0": run_r0}, 4)
+        record_flags("prefill", [ws])
         t_s, t_c, t_r0 = t["serial"], t["conc"], t["r0"]
         f = call_flops(N, K, w["rank"], M)
         out[f"{K}->{N} M={M}"] = {
@@ -374,6 +392,7 @@ def llama70b_context(torch, device):
                                                       main_stream=s),
                 "r0": lambda i, s: spear.spear_linear(sets[i % n_sets][si].without_compensator(), x,
                                                       y=y, workspace=ws, main_stream=s)}, n_sets)
+            record_flags("llama70b", [ws])
             t_ec, t_r0 = t["ec"], t["r0"]
             b, f = call_bytes(N, K, K, r, M), call_flops(N, K, r, M)
             gbs, tfs = b / (t_ec * 1e-3) / 1e9, f / (t_ec * 1e-3) / 1e12
@@ -418,6 +437,7 @@ def rank_gate_context(torch, device):
             t = graph_times_ms(torch, {"rank_gate": variant(lambda l: with_gate(l, rg)),
                                        "scalar_gate": variant(lambda l: l),
                                        "r0": variant(lambda l: l.without_compensator())}, n_sets)
+            record_flags("rank_gate", [ws])
             out[f"{K}->{N} M={M}"] = {
                 "us_rank_gate": round(t["rank_gate"] * 1e3, 2), "us_scalar_gate": round(t["scalar_gate"] * 1e3, 2),
                 "us_r0": round(t["r0"] * 1e3, 2),
@@ -518,6 +538,7 @@ def serving_context(torch, device):
                                                      "merged": round(measured(C, ecs, merged=True), 3)}
                                             for C in chunks}
         out["densities"][str(d)] = rec
+    record_flags("serving", [ws])
     del stack, plain, xs, ys, ws, wbuf
     torch.cuda.empty_cache()
     return out
@@ -932,6 +953,7 @@ def main():
     n_sets, rot_bytes = wl.n_sets, wl.rotation_bytes
     log(f"{n_sets} layer-set copies, rotation {rot_bytes / 2**30:.2f} GiB")
     total_ms, wall, cls_ms, classes = timed_decode_steps(torch, wl, args.steps, args.warmup)
+    record_flags("decode", wl.ws)
     ms_per_step = total_ms / args.steps
     value = wl.step_bytes * args.steps / (total_ms * 1e-3) / 1e9
     log(f"decode: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s")
@@ -969,6 +991,7 @@ def main():
         log("overhead vs rank 0")
         wl0 = DecodeWorkload(dev, rank_override=0)
         extra["decode_overhead_vs_rank0"] = decode_overhead(torch, wl, wl0)
+        record_flags("decode_overhead", wl.ws + wl0.ws)
         del wl0
         torch.cuda.empty_cache()
         log("prefill context")
@@ -998,9 +1021,12 @@ def main():
                                "gate; fp16 x N(0,1) with 1% channels x20",
                    "step": "12 compensated decode calls, graph-replayed",
                    "layer_copies": n_sets, "rotation_GiB": round(rot_bytes / 2**30, 3)},
-        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+        "roofline": roofline, "cpu_baseline": cpu, "workspace_flags": WS_FLAGS, "extra": extra,
     }
     print(json.dumps(line), flush=True)
+    if any(WS_FLAGS.values()):
+        log("a workspace error flag is set: the timings above ran a fallback path")
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -340,22 +340,40 @@ def test_decode_workspace_reuse_many_calls():
     assert _ws_header(ws) == [0] * 12
 
 
+def _sentinel_past(ws, offset):
+    """Fill the workspace from `offset` on with 0xFF bytes (fp32 NaN); returns a checker that
+    tells whether any of those bytes was overwritten."""
+    ws[offset:].fill_(255)
+
+    def written():
+        torch.cuda.synchronize()
+        return bool((ws[offset:] != 255).any().item())
+    return written
+
+
 def test_decode_split_needs_room_in_the_workspace():
     """K >= 8192 at 16 tokens takes the split-K launch when the workspace holds its
     partial tiles, and the unsplit launch when it holds only what that needs; both
-    match the oracle."""
+    match the oracle.  Which launch ran is observed: the split launch writes its partial
+    tiles past the unsplit launch's part of the workspace, the unsplit launch never does."""
     note("decode split-K fallback on a small workspace")
     hl, xb, lay, x = _setup(256, 8192, 128, 32, seed=61, M=16, outliers=True)
     ref = oracle_y(hl, xb)
     big = spear.new_workspace(lay, 16)
+    unsplit_need = spear.spear_linear_plan(lay, 16, big.numel())["workspace_bytes"]
     # the unsplit launch needs the header and the producers' partials: 3 row blocks
     # of [A; w_g] x 4 K-splits x 16 rows x 16 tokens x 4 bytes = 12288 bytes; the
     # split launch adds 2 tiles x 8 K-splits x 8 waves x 64 lanes x 16 bytes = 131072
+    assert unsplit_need == WS_HEADER_BYTES + 12288
     small = big[: WS_HEADER_BYTES + 12288 + 65536]
+    assert spear.spear_linear_plan(lay, 16, big.numel())["path"] == "decode_split"
+    assert spear.spear_linear_plan(lay, 16, small.numel())["path"] == "decode"
+    written = _sentinel_past(big, unsplit_need)
     y_split = spear.spear_linear_decode(lay, x, workspace=big)
-    torch.cuda.synchronize()
+    assert written(), "the split-K launch left its partial tiles unwritten"
+    written = _sentinel_past(small, unsplit_need)
     y_plain = spear.spear_linear_decode(lay, x, workspace=small)
-    torch.cuda.synchronize()
+    assert not written(), "the unsplit launch wrote past its part of the workspace"
     assert_close(gpu_y_f64(y_split, "f16"), ref, "split")
     assert_close(gpu_y_f64(y_plain, "f16"), ref, "unsplit")
     assert _ws_header(big) == [0] * 12
@@ -366,14 +384,19 @@ def test_decode_split_needs_room_in_the_workspace():
 @pytest.mark.parametrize("M", [1, 2, 8])
 def test_decode_long_k_default_thresholds(M):
     """K = 20480 >= twice the column threshold: the default thresholds take the split-K
-    launch from 2 tokens on and the one-launch kernel at 1; both match the oracle."""
+    launch from 2 tokens on and the one-launch kernel at 1; both match the oracle, and
+    the launch taken is observed through the workspace bytes it writes."""
     note(f"decode long K default thresholds M={M}")
     assert spear.spear_get_decode_split_min_m() == 16
     assert spear.spear_get_decode_split_min_k() == 8192
     hl, xb, lay, x = _setup(384, 20480, 0, 24, seed=71 + M, M=M, outliers=True)
     ws = spear.new_workspace(lay, M)
+    plan = spear.spear_linear_plan(lay, M, ws.numel())
+    assert plan["path"] == ("decode" if M == 1 else "decode_split")
+    unsplit_need = plan["workspace_bytes"]  # the least this call accepts: the unsplit launch's
+    written = _sentinel_past(ws, unsplit_need)
     y = spear.spear_linear_decode(lay, x, workspace=ws)
-    torch.cuda.synchronize()
+    assert written() == (M > 1)
     assert_close(gpu_y_f64(y, "f16"), oracle_y(hl, xb), f"long K M={M}")
     assert _ws_header(ws) == [0] * 12
 
@@ -593,19 +616,27 @@ def test_llama7b_prefill_sampled(K, N, schedule):
     assert_close(gpu_y_f64(y, "bf16")[np.ix_(toks, rows)], ref, f"7B prefill {K}->{N}")
 
 
-@pytest.mark.parametrize("schedule", ["serial", "concurrent"])
-def test_llama70b_layer_sampled(schedule):
+@pytest.mark.parametrize("K,N", synth.LLAMA70B_SHAPES)
+def test_llama70b_layer_sampled(K, N):
+    """Every Llama-70B projection (per-channel, rank 64, fp16) at the token counts the bench
+    times (1, 64, 256) and at 2 and 4 (the long-K split-K decode launch), through the
+    phase-aware entry point; prefill in both schedules.  After each call the workspace's
+    flags and counters are back at zero."""
     w = synth.WORKLOADS["llama70b-layer"]
-    K, N = 8192, 28672
-    hl = synth.make_layer(N, K, w["group_size"], w["rank"], seed=w["seed"], dtype="f16")
+    hl = synth.make_layer(N, K, w["group_size"], w["rank"], seed=w["seed"] + K + N, dtype="f16")
     lay = spear.layer_to_device(hl, DEV)
-    rows = sample_rows(N, 96, seed=70)
-    for M in w["tokens"]:
-        note(f"llama70b K={K} N={N} M={M} {schedule}")
+    rows = sample_rows(N, 96, seed=70 + K)
+    for M in (1, 2, 4) + tuple(m for m in w["tokens"] if m > 1):
         xb = synth.make_activations(M, K, seed=w["seed"] + M)
         x = spear.act_to_device(xb, "f16", DEV)
         ws = spear.new_workspace(lay, M)
-        aux = torch.cuda.Stream() if schedule == "concurrent" else None
-        y = spear.spear_linear(lay, x, workspace=ws, aux_stream=aux)
-        torch.cuda.synchronize()
-        assert_close(gpu_y_f64(y, "f16")[:, rows], oracle_y(hl, xb, rows=rows), f"70B M={M}")
+        ref = oracle_y(hl, xb, rows=rows)
+        for schedule in (("serial",) if M <= 32 else ("serial", "concurrent")):
+            note(f"llama70b K={K} N={N} M={M} {schedule} "
+                 f"{spear.spear_linear_plan(lay, M, ws.numel())['path']}")
+            aux = torch.cuda.Stream() if schedule == "concurrent" else None
+            y = spear.spear_linear(lay, x, workspace=ws, aux_stream=aux)
+            torch.cuda.synchronize()
+            assert_close(gpu_y_f64(y, "f16")[:, rows], ref, f"70B {K}->{N} M={M} {schedule}")
+            assert spear.spear_workspace_flags(ws) == 0
+            assert _ws_header(ws) == [0] * 12
