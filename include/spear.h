@@ -219,6 +219,19 @@ spear_status_t spear_set_decode_split_min_k(int32_t k);
 int32_t spear_get_decode_split_min_k(void);
 
 /*
+ * How long a decode launch's consumer workgroups wait for its compensator
+ * producers: at most `polls` reads of the producers' count (default 2^20,
+ * about a second).  If the wait expires, the workgroup computes the sums
+ * A x and w_g . x itself from A, w_g and x, so the output is the same up to
+ * the order of fp32 additions, and bit 0 of the workspace flags is set (see
+ * spear_workspace_flags).  0 makes every consumer compute them itself without
+ * waiting (for tests of that path; it is slow).  Process-wide; read when a
+ * call is issued (a captured graph keeps the value it was captured with).
+ */
+spear_status_t spear_set_decode_spin_limit(uint32_t polls);
+uint32_t spear_get_decode_spin_limit(void);
+
+/*
  * Chunk selector (2.2 C), host only: among n candidate prefill chunk sizes
  * with predicted step latencies pred_ms (host arrays), return the largest
  * chunk whose prediction is <= budget_ms (compared in float).  If none fits,
@@ -268,8 +281,10 @@ const char *spear_last_error(void);
 /*
  * Sticky error word of a workspace (device pointer), copied to *flags
  * (host) with a synchronous read on `stream`.  Bit 0 set: a decode launch
- * gave up waiting for its compensator producers (bounded wait).  Diagnostic
- * only; this call synchronises the stream.
+ * gave up waiting for its compensator producers (bounded wait, see
+ * spear_set_decode_spin_limit) and computed their sums itself; its output is
+ * still complete.  The bit stays set until the caller clears the word.
+ * Diagnostic only; this call synchronises the stream.
  */
 spear_status_t spear_workspace_flags(const void *workspace, uint32_t *flags,
                                      spear_stream_t stream);

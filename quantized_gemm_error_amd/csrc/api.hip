@@ -258,6 +258,13 @@ spear_status_t spear_set_decode_split_min_k(int32_t k) {
 
 int32_t spear_get_decode_split_min_k(void) { return get_decode_split_min_k(); }
 
+spear_status_t spear_set_decode_spin_limit(uint32_t polls) {
+  set_decode_spin_limit(polls);
+  return ok();
+}
+
+uint32_t spear_get_decode_spin_limit(void) { return get_decode_spin_limit(); }
+
 int32_t spear_select_chunk(const int32_t *chunks, const float *pred_ms, int32_t n, float budget_ms,
                            int32_t *violated) {
   if (!chunks || !pred_ms || n < 1) {

@@ -27,6 +27,11 @@ bool four_waves(const LayerDesc &L, int M) { return M <= 4 && L.K <= 4096; }
 std::atomic<int> g_split_min_m{16};
 std::atomic<int> g_split_min_k{8192};
 
+// Polls of the producers' count before a consumer computes the compensator's
+// projections itself (a poll with a short sleep takes about a microsecond
+// under load, so the default allows about a second).
+std::atomic<uint32_t> g_spin_limit{1u << 20};
+
 }  // namespace
 
 // Split-K wanted for M tokens at K columns (its plan must still fit and the
@@ -41,6 +46,9 @@ bool decode_split_wanted(int M, int K) {
   const int long_k_min = (mm + 7) / 8 < 2 ? 2 : (mm + 7) / 8;
   return M >= mm || ((long long)K >= 2LL * mk && M >= long_k_min);
 }
+
+void set_decode_spin_limit(uint32_t polls) { g_spin_limit.store(polls); }
+uint32_t get_decode_spin_limit() { return g_spin_limit.load(); }
 
 void set_decode_split_min_m(int m) { g_split_min_m.store(m); }
 int get_decode_split_min_m() { return g_split_min_m.load(); }

@@ -89,6 +89,8 @@ void set_decode_split_min_m(int m);
 int get_decode_split_min_m();
 void set_decode_split_min_k(int k);
 int get_decode_split_min_k();
+void set_decode_spin_limit(uint32_t polls);
+uint32_t get_decode_spin_limit();
 
 #define SPEAR_DECODE_VARIANT_API                                                          \
   DecodePlan plan_decode(const LayerDesc &L, int M);                                      \

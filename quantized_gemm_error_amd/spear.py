@@ -32,7 +32,7 @@ EXPORTED = (
     "spear_set_decode_split_min_m", "spear_get_decode_split_min_m",
     "spear_set_decode_split_min_k", "spear_get_decode_split_min_k", "spear_select_chunk",
     "spear_status_string", "spear_last_error", "spear_workspace_flags", "spear_version",
-    "spear_linear_plan",
+    "spear_linear_plan", "spear_set_decode_spin_limit", "spear_get_decode_spin_limit",
 )
 
 SPEAR_PATH_NONE = 0
@@ -124,6 +124,10 @@ def load_library(path: str = LIB_PATH):
     lib.spear_version.restype = i32
     lib.spear_linear_plan.argtypes = [LP, i32, sz, i32, ctypes.POINTER(SpearPlanC)]
     lib.spear_linear_plan.restype = i32
+    lib.spear_set_decode_spin_limit.argtypes = [ctypes.c_uint32]
+    lib.spear_set_decode_spin_limit.restype = i32
+    lib.spear_get_decode_spin_limit.argtypes = []
+    lib.spear_get_decode_spin_limit.restype = ctypes.c_uint32
     _lib = lib
     return lib
 
@@ -364,6 +368,14 @@ def spear_set_decode_split_min_k(k: int) -> None:
 
 def spear_get_decode_split_min_k() -> int:
     return int(load_library().spear_get_decode_split_min_k())
+
+
+def spear_set_decode_spin_limit(polls: int) -> None:
+    _check(load_library().spear_set_decode_spin_limit(int(polls)))
+
+
+def spear_get_decode_spin_limit() -> int:
+    return int(load_library().spear_get_decode_spin_limit())
 
 
 def spear_select_chunk(chunks, pred_ms, budget_ms: float):

@@ -272,3 +272,11 @@ def test_workspace_holds_only_the_partials_a_call_can_split_into(lib):
         need = lib.spear_workspace_bytes(ctypes.byref(lay), M)
         plan = _plan(lay, M, need)
         assert plan["workspace_bytes"] <= need
+
+
+def test_decode_spin_limit_setting(lib):
+    assert spear.spear_get_decode_spin_limit() == 1 << 20
+    spear.spear_set_decode_spin_limit(0)
+    assert spear.spear_get_decode_spin_limit() == 0
+    spear.spear_set_decode_spin_limit(1 << 20)
+    assert spear.spear_get_decode_spin_limit() == 1 << 20

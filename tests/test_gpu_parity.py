@@ -147,6 +147,53 @@ def test_decode_parity(N, K, G, r, M, dtype, outl, split_min):
     assert _ws_header(ws) == [0] * 12
 
 
+@contextlib.contextmanager
+def decode_spin_limit(polls):
+    old = spear.spear_get_decode_spin_limit()
+    spear.spear_set_decode_spin_limit(polls)
+    try:
+        yield
+    finally:
+        spear.spear_set_decode_spin_limit(old)
+
+
+EXPIRY_CASES = [
+    # N, K, G, r, M, dtype, split_min, rank-gate hidden (0: scalar gate)
+    (512, 512, 0, 16, 1, "f16", 33, 0),        # the small layer, one token, 4-wave launch
+    (130, 640, 128, 32, 17, "f16", 33, 0),     # two token blocks, ragged
+    (64, 2048, 128, 64, 32, "bf16", 33, 0),    # chunked staging (x not in LDS whole)
+    (160, 1024, 128, 128, 32, "f16", 33, 0),   # the largest rank
+    (300, 2048, 0, 24, 17, "bf16", 1, 0),      # the split-K launch
+    (200, 1024, 128, 32, 5, "f16", 33, 16),    # the per-rank gate
+    (96, 512, 128, 40, 32, "f16", 1, 64),      # the per-rank gate, split-K launch
+]
+
+
+@pytest.mark.parametrize("N,K,G,r,M,dtype,split_min,hidden", EXPIRY_CASES)
+def test_decode_wait_expiry_computes_the_sums_itself(N, K, G, r, M, dtype, split_min, hidden):
+    """With no wait for the producers at all (spin limit 0, set on the host), every consumer
+    workgroup computes [A; w_g] x itself: the output still matches the oracle, and bit 0 of
+    the workspace flags records the expiry.  Every kernel exits normally."""
+    note(f"wait expiry N={N} K={K} r={r} M={M} {dtype} split_min={split_min} hidden={hidden}")
+    hl, xb, lay, x = _setup(N, K, G, r, seed=N + K + M + 5, dtype=dtype, M=M, outliers=True,
+                            b_gate=0.3)
+    params = None
+    if hidden:
+        params = synth.make_rank_gate(r, hidden, seed=N + r, t_scale=0.01 * np.sqrt(K))
+        lay.rank_gate = spear.rank_gate_to_device(params, 0.9, DEV)
+    with decode_split_min_m(split_min), decode_spin_limit(0):
+        ws = spear.new_workspace(lay, M)
+        assert spear.spear_linear_plan(lay, M, ws.numel())["path"] == \
+            ("decode_split" if split_min == 1 else "decode")
+        y = spear.spear_linear_decode(lay, x, workspace=ws)
+        torch.cuda.synchronize()
+    ref = _rank_gate_ref(hl, xb, params, 0.9) if hidden else oracle_y(hl, xb)
+    assert_close(gpu_y_f64(y, dtype), ref, "self-computed compensator")
+    assert spear.spear_workspace_flags(ws) & 1
+    hdr = _ws_header(ws)
+    assert hdr[0] == 0 and hdr[2:] == [0] * 10   # counters reset; only the flags word is set
+
+
 @pytest.mark.parametrize("M", [1, 4, 16, 32])
 def test_decode_gate_off_is_rank_zero_bitwise(M):
     note(f"gate off M={M}")
