@@ -176,6 +176,27 @@ spear_status_t spear_linear_decode(const spear_layer_t *layer, spear_dtype_t dty
                                    size_t workspace_bytes, spear_stream_t stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same
+ * call as spear_linear_decode, without a workspace argument: its workspace
+ * is a device array of SPEAR_NOALLOC_SCRATCH_BYTES held by the library, one
+ * per GPU (the GPU current when the call is made, which must be the stream's),
+ * for as long as the process runs.  Nothing is allocated, by the call or by
+ * its set-up (the first call on a GPU finds the array's address and clears
+ * its counters with a kernel on `stream`).  Every call on one GPU shares that
+ * array: calls that overlap on one GPU (concurrent streams) race and must not
+ * be issued; stream-ordered calls are fine, as each call leaves the counters
+ * at zero for the next.  A call whose workspace need exceeds the array
+ * returns SPEAR_ERR_WORKSPACE; a split-K launch whose partial tiles do not
+ * fit runs the unsplit launch instead (never at the sizes the library
+ * supports: the largest need is below 16.2 MiB).
+ */
+#define SPEAR_NOALLOC_SCRATCH_BYTES (17u << 20)
+spear_status_t spear_linear_decode_noalloc(const spear_layer_t *layer, spear_dtype_t dtype,
+                                           const void *x, void *y, int32_t M,
+                                           spear_stream_t stream);
+
+/*
  * Prefill path (2.2 A, prefill phase): any M >= 1.  The 4-bit product runs on
  * main_stream as an MFMA GEMM over LDS-staged dequantized tiles; the
  * compensator's thin products (gate, A x, scaled by the gate) run on

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "internal.h"
 
@@ -125,6 +126,53 @@ spear_status_t hip_status(hipError_t e, const char *what) {
   return ok();
 }
 
+// The no-allocation decode entry point's workspace: one array per GPU, in
+// this file's device code object, zero when loaded.  In host code `scratch`
+// names a host-side stand-in, never the device array: host code only ever
+// uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[SPEAR_NOALLOC_SCRATCH_BYTES];
+
+static_assert(SPEAR_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Zeroes n 32-bit words (the workspace header's counters).
+__global__ void clear_words(uint32_t *p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The current device's scratch address.  Set-up, once per device with that
+// device current: look the array up (no allocation) and clear its header
+// with a kernel on `stream`, ordered before the call's own launch.
+spear_status_t noalloc_scratch(hipStream_t stream, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPEAR_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SPEAR_ERR_UNSUPPORTED, "device %d: the no-allocation path serves devices 0..%d",
+                dev, kMaxDevices - 1);
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(SPEAR_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      const int words = (int)(kWsDataOff / sizeof(uint32_t));
+      hipLaunchKernelGGL(clear_words, dim3(4), dim3(256), 0, stream, (uint32_t *)p, words);
+      if ((e = hipGetLastError()) != hipSuccess)
+        return fail(SPEAR_ERR_HIP, "scratch set-up on device %d: %s", dev, hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SPEAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,6 +217,30 @@ spear_status_t spear_linear_decode(const spear_layer_t *layer, spear_dtype_t dty
   return hip_status(launch_decode(d, (int)dtype, (const uint16_t *)x, (uint16_t *)y, M, workspace,
                                   aligned(workspace, 256) ? workspace_bytes : 0,
                                   (hipStream_t)stream),
+                    "decode launch");
+}
+
+spear_status_t spear_linear_decode_noalloc(const spear_layer_t *layer, spear_dtype_t dtype,
+                                           const void *x, void *y, int32_t M,
+                                           spear_stream_t stream) {
+  LayerDesc d;
+  spear_status_t st = check_layer(layer, &d);
+  if (st != SPEAR_OK) return st;
+  if (M < 0 || M > SPEAR_MAX_DECODE_M)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode M=%d outside 0..%d", M, SPEAR_MAX_DECODE_M);
+  if (M == 0) return ok();
+  if ((st = check_io(dtype, x, y)) != SPEAR_OK) return st;
+  if (!decode_supported(d, M))
+    return fail(SPEAR_ERR_UNSUPPORTED, "no decode launch shape fits K=%d G=%d M=%d", d.K, d.G, M);
+  const size_t need = decode_workspace_bytes(d, M);
+  if (need > (size_t)SPEAR_NOALLOC_SCRATCH_BYTES)
+    return fail(SPEAR_ERR_WORKSPACE,
+                "decode needs %zu bytes of workspace; the no-allocation scratch holds %zu", need,
+                (size_t)SPEAR_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if ((st = noalloc_scratch((hipStream_t)stream, &ws)) != SPEAR_OK) return st;
+  return hip_status(launch_decode(d, (int)dtype, (const uint16_t *)x, (uint16_t *)y, M, ws,
+                                  SPEAR_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream),
                     "decode launch");
 }
 

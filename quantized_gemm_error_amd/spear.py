@@ -33,7 +33,9 @@ EXPORTED = (
     "spear_set_decode_split_min_k", "spear_get_decode_split_min_k", "spear_select_chunk",
     "spear_status_string", "spear_last_error", "spear_workspace_flags", "spear_version",
     "spear_linear_plan", "spear_set_decode_spin_limit", "spear_get_decode_spin_limit",
+    "spear_linear_decode_noalloc",
 )
+SPEAR_NOALLOC_SCRATCH_BYTES = 17 << 20
 
 SPEAR_PATH_NONE = 0
 SPEAR_PATH_DECODE = 1
@@ -95,6 +97,8 @@ def load_library(path: str = LIB_PATH):
     lib.spear_pack_int4.restype = i32
     lib.spear_linear_decode.argtypes = [LP, i32, P, P, i32, P, sz, P]
     lib.spear_linear_decode.restype = i32
+    lib.spear_linear_decode_noalloc.argtypes = [LP, i32, P, P, i32, P]
+    lib.spear_linear_decode_noalloc.restype = i32
     lib.spear_linear_prefill.argtypes = [LP, i32, P, P, i32, P, sz, P, P]
     lib.spear_linear_prefill.restype = i32
     lib.spear_linear.argtypes = [LP, i32, P, P, i32, P, sz, P, P]
@@ -322,6 +326,16 @@ def spear_linear_decode(layer: SpearLayer, x, y=None, workspace=None, stream=Non
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().spear_linear_decode(ctypes.byref(c), _dtype_code(x), _ptr(x), _ptr(y), M,
                                               _ptr(workspace), ws_bytes, _stream(stream)))
+    return y
+
+
+def spear_linear_decode_noalloc(layer: SpearLayer, x, y=None, stream=None):
+    """spear_linear_decode on the library's own per-GPU scratch (no workspace, no allocation
+    by the library; y is allocated here only when not given)."""
+    M, y = _io(layer, x, y)
+    c = layer.as_c()
+    _check(load_library().spear_linear_decode_noalloc(ctypes.byref(c), _dtype_code(x), _ptr(x),
+                                                      _ptr(y), M, _stream(stream)))
     return y
 
 
