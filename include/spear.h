@@ -219,6 +219,40 @@ spear_status_t spear_linear(const spear_layer_t *layer, spear_dtype_t dtype, con
                             void *y, int32_t M, void *workspace, size_t workspace_bytes,
                             spear_stream_t main_stream, spear_stream_t aux_stream);
 
+/*
+ * Static graph of layer calls (2.2 A, prefill phase: the compensator runs as
+ * a separate kernel beside the GEMM in a static graph, so no host launch
+ * overhead sits between the kernels).  The library captures a sequence of
+ * spear_linear calls into one HIP graph it holds; each prefill call's
+ * compensator kernels go on the graph's own aux branch (forked from and
+ * joined back into the main chain), decode calls are single launches.
+ * Calls run in the order they were added.  Every pointer given to
+ * spear_graph_add (x, y, the layer's arrays, the workspace) is baked into the
+ * graph: each launch reads and writes those same buffers, which must stay
+ * allocated until the graph is destroyed; their contents may change between
+ * launches.  Two launches of one graph, or of graphs that share a workspace,
+ * must be ordered (the same stream, or events).
+ *
+ *   spear_graph_begin   starts a graph (creates the library's capture and aux
+ *                       streams, default priority); *graph receives the handle.
+ *   spear_graph_add     validates and appends one spear_linear call, with the
+ *                       same arguments and checks (nothing runs yet).  An
+ *                       invalid call returns its error and adds nothing.
+ *   spear_graph_end     instantiates the graph; after it only launch and
+ *                       destroy are valid.
+ *   spear_graph_launch  runs the whole graph once on `stream`, asynchronously.
+ *   spear_graph_destroy releases the graph (any state; NULL is a no-op).
+ * The graph is host-side state owned by the caller through the handle.
+ */
+typedef struct spear_graph *spear_graph_t;
+spear_status_t spear_graph_begin(spear_graph_t *graph);
+spear_status_t spear_graph_add(spear_graph_t graph, const spear_layer_t *layer,
+                               spear_dtype_t dtype, const void *x, void *y, int32_t M,
+                               void *workspace, size_t workspace_bytes);
+spear_status_t spear_graph_end(spear_graph_t graph);
+spear_status_t spear_graph_launch(spear_graph_t graph, spear_stream_t stream);
+spear_status_t spear_graph_destroy(spear_graph_t graph);
+
 /* Dispatch threshold for spear_linear, 1..SPEAR_MAX_DECODE_M (default 32). Process-wide. */
 spear_status_t spear_set_decode_max_m(int32_t m);
 int32_t spear_get_decode_max_m(void);

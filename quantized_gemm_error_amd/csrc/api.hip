@@ -303,6 +303,87 @@ spear_status_t spear_linear_plan(const spear_layer_t *layer, int32_t M, size_t w
   return ok();
 }
 
+}  // extern "C"
+
+// A graph under construction (capturing on its own stream) or instantiated.
+struct spear_graph {
+  hipStream_t main = nullptr, aux = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  bool capturing = false;
+  int calls = 0;
+};
+
+namespace {
+
+void graph_release(spear_graph *g) {
+  if (g->capturing) {  // abandon the capture
+    hipGraph_t tmp = nullptr;
+    if (hipStreamEndCapture(g->main, &tmp) == hipSuccess && tmp) (void)hipGraphDestroy(tmp);
+    (void)hipGetLastError();
+  }
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  if (g->aux) (void)hipStreamDestroy(g->aux);
+  if (g->main) (void)hipStreamDestroy(g->main);
+}
+
+}  // namespace
+
+extern "C" {
+
+spear_status_t spear_graph_begin(spear_graph_t *graph) {
+  if (!graph) return fail(SPEAR_ERR_INVALID_ARGUMENT, "graph must not be NULL");
+  *graph = nullptr;
+  spear_graph *g = new spear_graph();
+  hipError_t e = hipStreamCreateWithFlags(&g->main, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&g->aux, hipStreamNonBlocking);
+  // relaxed: the calling thread may make other HIP calls while the graph is built
+  if (e == hipSuccess) e = hipStreamBeginCapture(g->main, hipStreamCaptureModeRelaxed);
+  if (e != hipSuccess) {
+    graph_release(g);
+    delete g;
+    return hip_status(e, "graph begin");
+  }
+  g->capturing = true;
+  *graph = g;
+  return ok();
+}
+
+spear_status_t spear_graph_add(spear_graph_t graph, const spear_layer_t *layer,
+                               spear_dtype_t dtype, const void *x, void *y, int32_t M,
+                               void *workspace, size_t workspace_bytes) {
+  if (!graph) return fail(SPEAR_ERR_INVALID_ARGUMENT, "graph must not be NULL");
+  if (!graph->capturing) return fail(SPEAR_ERR_INVALID_ARGUMENT, "graph already ended");
+  const spear_status_t st = spear_linear(layer, dtype, x, y, M, workspace, workspace_bytes,
+                                         graph->main, graph->aux);
+  if (st == SPEAR_OK) ++graph->calls;
+  return st;
+}
+
+spear_status_t spear_graph_end(spear_graph_t graph) {
+  if (!graph) return fail(SPEAR_ERR_INVALID_ARGUMENT, "graph must not be NULL");
+  if (!graph->capturing) return fail(SPEAR_ERR_INVALID_ARGUMENT, "graph already ended");
+  graph->capturing = false;
+  hipError_t e = hipStreamEndCapture(graph->main, &graph->graph);
+  if (e != hipSuccess) return hip_status(e, "graph capture");
+  e = hipGraphInstantiate(&graph->exec, graph->graph, nullptr, nullptr, 0);
+  return hip_status(e, "graph instantiate");
+}
+
+spear_status_t spear_graph_launch(spear_graph_t graph, spear_stream_t stream) {
+  if (!graph) return fail(SPEAR_ERR_INVALID_ARGUMENT, "graph must not be NULL");
+  if (!graph->exec) return fail(SPEAR_ERR_INVALID_ARGUMENT, "graph not ended");
+  return hip_status(hipGraphLaunch(graph->exec, (hipStream_t)stream), "graph launch");
+}
+
+spear_status_t spear_graph_destroy(spear_graph_t graph) {
+  if (!graph) return ok();
+  graph_release(graph);
+  delete graph;
+  return ok();
+}
+
 spear_status_t spear_set_decode_max_m(int32_t m) {
   if (m < 1 || m > SPEAR_MAX_DECODE_M)
     return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode_max_m=%d outside 1..%d", m, SPEAR_MAX_DECODE_M);

@@ -33,7 +33,8 @@ EXPORTED = (
     "spear_set_decode_split_min_k", "spear_get_decode_split_min_k", "spear_select_chunk",
     "spear_status_string", "spear_last_error", "spear_workspace_flags", "spear_version",
     "spear_linear_plan", "spear_set_decode_spin_limit", "spear_get_decode_spin_limit",
-    "spear_linear_decode_noalloc",
+    "spear_linear_decode_noalloc", "spear_graph_begin", "spear_graph_add", "spear_graph_end",
+    "spear_graph_launch", "spear_graph_destroy",
 )
 SPEAR_NOALLOC_SCRATCH_BYTES = 17 << 20
 
@@ -99,6 +100,16 @@ def load_library(path: str = LIB_PATH):
     lib.spear_linear_decode.restype = i32
     lib.spear_linear_decode_noalloc.argtypes = [LP, i32, P, P, i32, P]
     lib.spear_linear_decode_noalloc.restype = i32
+    lib.spear_graph_begin.argtypes = [ctypes.POINTER(P)]
+    lib.spear_graph_begin.restype = i32
+    lib.spear_graph_add.argtypes = [P, LP, i32, P, P, i32, P, sz]
+    lib.spear_graph_add.restype = i32
+    lib.spear_graph_end.argtypes = [P]
+    lib.spear_graph_end.restype = i32
+    lib.spear_graph_launch.argtypes = [P, P]
+    lib.spear_graph_launch.restype = i32
+    lib.spear_graph_destroy.argtypes = [P]
+    lib.spear_graph_destroy.restype = i32
     lib.spear_linear_prefill.argtypes = [LP, i32, P, P, i32, P, sz, P, P]
     lib.spear_linear_prefill.restype = i32
     lib.spear_linear.argtypes = [LP, i32, P, P, i32, P, sz, P, P]
@@ -358,6 +369,46 @@ def spear_linear(layer: SpearLayer, x, y=None, workspace=None, main_stream=None,
     _check(load_library().spear_linear(ctypes.byref(c), _dtype_code(x), _ptr(x), _ptr(y), M,
                                        _ptr(workspace), ws_bytes, _stream(main_stream), aux))
     return y
+
+
+class SpearGraph:
+    """A static graph of layer calls held by the library (spear_graph_*): add calls with
+    add(), then end(), then launch() as often as needed.  The tensors given to add() are
+    kept referenced here, since the graph reads and writes them on every launch."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(load_library().spear_graph_begin(ctypes.byref(h)))
+        self._h = h
+        self._keep = []
+
+    def add(self, layer: SpearLayer, x, y=None, workspace=None):
+        M, y = _io(layer, x, y, workspace)
+        c = layer.as_c()
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(load_library().spear_graph_add(self._h, ctypes.byref(c), _dtype_code(x), _ptr(x),
+                                              _ptr(y), M, _ptr(workspace), ws_bytes))
+        self._keep.append((layer, x, y, workspace))
+        return y
+
+    def end(self):
+        _check(load_library().spear_graph_end(self._h))
+        return self
+
+    def launch(self, stream=None):
+        _check(load_library().spear_graph_launch(self._h, _stream(stream)))
+
+    def destroy(self):
+        if self._h is not None:
+            _check(load_library().spear_graph_destroy(self._h))
+            self._h = None
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
 
 
 def spear_set_decode_max_m(m: int) -> None:

@@ -280,3 +280,12 @@ def test_decode_spin_limit_setting(lib):
     assert spear.spear_get_decode_spin_limit() == 0
     spear.spear_set_decode_spin_limit(1 << 20)
     assert spear.spear_get_decode_spin_limit() == 1 << 20
+
+
+def test_graph_calls_reject_null_handles(lib):
+    assert lib.spear_graph_begin(None) == 1
+    assert lib.spear_graph_add(None, ctypes.byref(_layer()), 0, FAKE * 2, FAKE * 3, 1, FAKE * 4,
+                               1 << 20) == 1
+    assert lib.spear_graph_end(None) == 1
+    assert lib.spear_graph_launch(None, None) == 1
+    assert lib.spear_graph_destroy(None) == 0
