@@ -397,7 +397,7 @@ def llama70b_context(torch, device):
             b, f = call_bytes(N, K, K, r, M), call_flops(N, K, r, M)
             gbs, tfs = b / (t_ec * 1e-3) / 1e9, f / (t_ec * 1e-3) / 1e12
             out[f"{K}->{N} M={M}"] = {
-                "phase": "decode" if M <= 32 else "prefill",
+                "phase": spear.spear_linear_plan(base[si], M, ws.numel())["path"],
                 "us_ec": round(t_ec * 1e3, 2), "us_r0": round(t_r0 * 1e3, 2),
                 "overhead_pct": round(100.0 * (t_ec / t_r0 - 1.0), 2),
                 "GBps_ec": round(gbs, 1), "hbm_frac_ec": round(gbs / HBM_PEAK_GBS, 4),

@@ -126,7 +126,7 @@ typedef struct spear_layer {
 
 #define SPEAR_MAX_RANK 128
 #define SPEAR_MAX_K 131072
-#define SPEAR_MAX_DECODE_M 32
+#define SPEAR_MAX_DECODE_M 128  /* 1..32: per-row-group kernels; 33..128: the wide-tile kernel */
 
 /*
  * Workspace bytes that spear_linear_decode, spear_linear_prefill and
@@ -159,7 +159,11 @@ spear_status_t spear_pack_int4(const uint8_t *q, int32_t *qweight, int64_t N, in
                                spear_stream_t stream);
 
 /*
- * Decode path (2.2 A, decode phase): one fused kernel for 1 <= M <= 32 tokens.
+ * Decode path (2.2 A, decode phase): one fused kernel launch for 1 <= M <= 128
+ * tokens.  Up to 32 tokens, workgroups own groups of 16 to 128 output rows
+ * over all of K (or K-splits, see below); from 33 tokens on, workgroups own
+ * tiles of 256 output rows over a K-split each and stream x through LDS, so
+ * that each staged activation fragment feeds many rows.
  * x [M][K] and y [M][N] are row-major activation-type device arrays, x and y
  * 16-byte aligned.  The gate, A x and the gated B (A x) term are computed in
  * the same launch as the 4-bit product and added before y is rounded.
@@ -253,15 +257,15 @@ spear_status_t spear_graph_end(spear_graph_t graph);
 spear_status_t spear_graph_launch(spear_graph_t graph, spear_stream_t stream);
 spear_status_t spear_graph_destroy(spear_graph_t graph);
 
-/* Dispatch threshold for spear_linear, 1..SPEAR_MAX_DECODE_M (default 32). Process-wide. */
+/* Dispatch threshold for spear_linear, 1..SPEAR_MAX_DECODE_M (default 64). Process-wide. */
 spear_status_t spear_set_decode_max_m(int32_t m);
 int32_t spear_get_decode_max_m(void);
 
 /*
  * When decode considers the split-K launch: for layers with
  * K >= spear_get_decode_split_min_k() (>= 1, default 8192), from
- * M = spear_get_decode_split_min_m() tokens on (1..SPEAR_MAX_DECODE_M + 1,
- * default 16; SPEAR_MAX_DECODE_M + 1 switches the split off), and, for layers
+ * M = spear_get_decode_split_min_m() tokens on (1..33, default 16; 33 switches
+ * the split off; these thresholds concern calls of at most 32 tokens), and, for layers
  * with K at least twice the column threshold, from an eighth of the token
  * threshold on but never below 2 tokens (M >= max(2, ceil(min_m / 8)); with
  * the defaults, M >= 2 from K = 16384).
@@ -306,7 +310,8 @@ typedef enum spear_path {
   SPEAR_PATH_NONE = 0,          /* M == 0: nothing is launched */
   SPEAR_PATH_DECODE = 1,        /* fused decode, one workgroup per group of output rows */
   SPEAR_PATH_DECODE_SPLIT = 2,  /* fused decode, K split across each 128-row tile's workgroups */
-  SPEAR_PATH_PREFILL = 3        /* the prefill GEMM path */
+  SPEAR_PATH_PREFILL = 3,       /* the prefill GEMM path */
+  SPEAR_PATH_DECODE_WIDE = 4    /* fused decode for 33..128 tokens: 256-row tiles over K-splits */
 } spear_path_t;
 
 typedef struct spear_plan {

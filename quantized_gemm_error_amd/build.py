@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libspear.so")
 
-SOURCES = ("api.hip", "pack.hip", "decode.hip", "decode_w8.hip", "decode_w4.hip", "prefill.hip")
+SOURCES = ("api.hip", "pack.hip", "decode.hip", "decode_w8.hip", "decode_w4.hip", "wide.hip",
+           "prefill.hip")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are switched off for all device code; hipcc then

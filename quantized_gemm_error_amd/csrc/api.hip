@@ -16,7 +16,13 @@ using namespace spear;
 namespace {
 
 thread_local char g_last_error[512] = "";
-std::atomic<int32_t> g_decode_max_m{SPEAR_MAX_DECODE_M};
+constexpr int32_t kSmallDecodeM = 32;  // the per-row-group decode kernels; past it, the wide one
+// spear_linear's dispatch threshold.  Measured on MI355X (compensated calls):
+// at 64 tokens the wide decode launch beats the prefill path on every Llama-7B
+// and Llama-70B projection (e.g. 8192 x 8192: 36.7 vs 49.8 us; 8192 -> 28672:
+// 67.9 vs 99.9 us); at 128 tokens the prefill path wins on most of them.
+constexpr int32_t kDefaultDecodeMaxM = 64;
+std::atomic<int32_t> g_decode_max_m{kDefaultDecodeMaxM};
 
 spear_status_t fail(spear_status_t st, const char *fmt, ...) {
   va_list ap;
@@ -126,6 +132,21 @@ spear_status_t hip_status(hipError_t e, const char *what) {
   return ok();
 }
 
+// Decode for M tokens (1..SPEAR_MAX_DECODE_M): whether a launch shape fits,
+// the least workspace, and the launch.
+bool decode_fits(const LayerDesc &d, int M) {
+  return M <= kSmallDecodeM ? decode_supported(d, M) : plan_wide(d, M).ok;
+}
+size_t decode_need(const LayerDesc &d, int M) {
+  return M <= kSmallDecodeM ? decode_workspace_bytes(d, M) : wide_workspace_bytes(d, M);
+}
+hipError_t decode_launch(const LayerDesc &d, int dtype, const void *x, void *y, int M, void *ws,
+                         size_t ws_bytes, hipStream_t s) {
+  if (M <= kSmallDecodeM)
+    return launch_decode(d, dtype, (const uint16_t *)x, (uint16_t *)y, M, ws, ws_bytes, s);
+  return launch_wide(d, dtype, (const uint16_t *)x, (uint16_t *)y, M, ws, s);
+}
+
 // The no-allocation decode entry point's workspace: one array per GPU, in
 // this file's device code object, zero when loaded.  In host code `scratch`
 // names a host-side stand-in, never the device array: host code only ever
@@ -183,8 +204,9 @@ size_t spear_workspace_bytes(const spear_layer_t *layer, int32_t M) {
   // enough for every call with 1..M tokens: both needs grow with M
   size_t need = prefill_workspace_bytes(d, M < 1 ? 1 : M);
   const int dm = M < 1 ? 1 : (M < SPEAR_MAX_DECODE_M ? M : SPEAR_MAX_DECODE_M);
-  for (int m = 1; m <= dm; ++m) {  // the split launch's needs vary with M's tile plan
-    const size_t dec = decode_fast_workspace_bytes(d, m);
+  for (int m = 1; m <= dm; ++m) {  // the split launches' needs vary with M's tile plan
+    const size_t dec = m <= kSmallDecodeM ? decode_fast_workspace_bytes(d, m)
+                                          : wide_workspace_bytes(d, m);
     if (dec > need) need = dec;
   }
   return need < 256 ? 256 : need;
@@ -210,11 +232,10 @@ spear_status_t spear_linear_decode(const spear_layer_t *layer, spear_dtype_t dty
     return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode M=%d outside 0..%d", M, SPEAR_MAX_DECODE_M);
   if (M == 0) return ok();
   if ((st = check_io(dtype, x, y)) != SPEAR_OK) return st;
-  if (!decode_supported(d, M))
+  if (!decode_fits(d, M))
     return fail(SPEAR_ERR_UNSUPPORTED, "no decode launch shape fits K=%d G=%d M=%d", d.K, d.G, M);
-  if ((st = check_ws(workspace, workspace_bytes, decode_workspace_bytes(d, M))) != SPEAR_OK)
-    return st;
-  return hip_status(launch_decode(d, (int)dtype, (const uint16_t *)x, (uint16_t *)y, M, workspace,
+  if ((st = check_ws(workspace, workspace_bytes, decode_need(d, M))) != SPEAR_OK) return st;
+  return hip_status(decode_launch(d, (int)dtype, x, y, M, workspace,
                                   aligned(workspace, 256) ? workspace_bytes : 0,
                                   (hipStream_t)stream),
                     "decode launch");
@@ -230,17 +251,17 @@ spear_status_t spear_linear_decode_noalloc(const spear_layer_t *layer, spear_dty
     return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode M=%d outside 0..%d", M, SPEAR_MAX_DECODE_M);
   if (M == 0) return ok();
   if ((st = check_io(dtype, x, y)) != SPEAR_OK) return st;
-  if (!decode_supported(d, M))
+  if (!decode_fits(d, M))
     return fail(SPEAR_ERR_UNSUPPORTED, "no decode launch shape fits K=%d G=%d M=%d", d.K, d.G, M);
-  const size_t need = decode_workspace_bytes(d, M);
+  const size_t need = decode_need(d, M);
   if (need > (size_t)SPEAR_NOALLOC_SCRATCH_BYTES)
     return fail(SPEAR_ERR_WORKSPACE,
                 "decode needs %zu bytes of workspace; the no-allocation scratch holds %zu", need,
                 (size_t)SPEAR_NOALLOC_SCRATCH_BYTES);
   void *ws = nullptr;
   if ((st = noalloc_scratch((hipStream_t)stream, &ws)) != SPEAR_OK) return st;
-  return hip_status(launch_decode(d, (int)dtype, (const uint16_t *)x, (uint16_t *)y, M, ws,
-                                  SPEAR_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream),
+  return hip_status(decode_launch(d, (int)dtype, x, y, M, ws, SPEAR_NOALLOC_SCRATCH_BYTES,
+                                  (hipStream_t)stream),
                     "decode launch");
 }
 
@@ -290,10 +311,13 @@ spear_status_t spear_linear_plan(const spear_layer_t *layer, int32_t M, size_t w
   // the workspace checks of the calls, with any non-null 256-byte aligned pointer
   void *const ws = workspace_bytes > 0 ? (void *)(uintptr_t)256 : nullptr;
   if (decode) {
-    if (!decode_supported(d, M))
+    if (!decode_fits(d, M))
       return fail(SPEAR_ERR_UNSUPPORTED, "no decode launch shape fits K=%d G=%d M=%d", d.K, d.G, M);
-    if ((st = check_ws(ws, workspace_bytes, decode_workspace_bytes(d, M))) != SPEAR_OK) return st;
-    describe_decode(d, M, workspace_bytes, plan);
+    if ((st = check_ws(ws, workspace_bytes, decode_need(d, M))) != SPEAR_OK) return st;
+    if (M <= kSmallDecodeM)
+      describe_decode(d, M, workspace_bytes, plan);
+    else
+      describe_wide(d, M, plan);
   } else {
     if ((ws || prefill_needs_workspace(d)) &&
         (st = check_ws(ws, workspace_bytes, prefill_workspace_bytes(d, M))) != SPEAR_OK)
@@ -394,9 +418,9 @@ spear_status_t spear_set_decode_max_m(int32_t m) {
 int32_t spear_get_decode_max_m(void) { return g_decode_max_m.load(); }
 
 spear_status_t spear_set_decode_split_min_m(int32_t m) {
-  if (m < 1 || m > SPEAR_MAX_DECODE_M + 1)
+  if (m < 1 || m > kSmallDecodeM + 1)
     return fail(SPEAR_ERR_INVALID_ARGUMENT, "decode_split_min_m=%d outside 1..%d", m,
-                SPEAR_MAX_DECODE_M + 1);
+                kSmallDecodeM + 1);
   set_decode_split_min_m(m);
   return ok();
 }

@@ -79,6 +79,24 @@ struct DecodePlan {
   size_t split_off, split_bytes;
 };
 
+// Launch geometry of the wide decode kernel (33..128 tokens, wide.hip).
+struct WidePlan {
+  bool ok;
+  int mb, r;             // 16-token blocks (4 or 8); 16-row blocks per wave
+  int rb_a, ks, producers, rp1;
+  int nb, n_tiles, ksp, nbs;
+  int buf_halves, red_off;
+  bool direct;           // rank 0, one split: the main kernel writes y itself
+  size_t lds;
+  size_t tp_off, u_off, part_off, end;  // workspace: [A; w_g] x sums, U, partial outputs
+};
+WidePlan plan_wide(const LayerDesc &L, int M);
+size_t wide_workspace_bytes(const LayerDesc &L, int M);
+void describe_wide(const LayerDesc &L, int M, spear_plan_t *out);
+hipError_t launch_wide(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
+                       void *ws, hipStream_t s);
+int wide_launches(const LayerDesc &L, int M);  // kernel launches of one wide call
+
 // Decode, dispatched per call to one of two compilations of the same kernels
 // (8 or 4 waves per workgroup; decode.hip picks).
 bool decode_supported(const LayerDesc &L, int M);
@@ -108,6 +126,12 @@ void describe_decode(const LayerDesc &L, int M, size_t ws_bytes, spear_plan_t *o
 void describe_prefill(const LayerDesc &L, int M, size_t ws_bytes, spear_plan_t *out);
 size_t prefill_workspace_bytes(const LayerDesc &L, int M);
 bool prefill_needs_workspace(const LayerDesc &L);  // false: optional (splits K when given)
+
+// prefill.hip kernels shared with the wide decode launch
+hipError_t launch_form_u(const LayerDesc &L, const float *Tp, int ks, int M, float *U,
+                         hipStream_t s);
+hipError_t launch_finish_parts(const LayerDesc &L, int dtype, uint16_t *y, int M, const float *part,
+                               int ks, const float *U, bool scale_rows, hipStream_t s);
 
 hipError_t launch_pack_int4(const uint8_t *q, int32_t *out, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,

@@ -989,6 +989,37 @@ static void launch_finish(const FinishArgs &f, dim3 grid, bool perch, bool ec, h
     hipLaunchKernelGGL((prefill_finish_kernel<DT, PARTS, false, false>), grid, dim3(256), 0, s, f);
 }
 
+// U = diag(g) (X A^T) (or the per-rank gate's U) [M][rp1] from K-split sums
+// [ks][M][rp1] of [A; w_g] x, each summed in split order.
+hipError_t launch_form_u(const LayerDesc &L, const float *Tp, int ks, int M, float *U,
+                         hipStream_t s) {
+  const int rp1 = rank_pad(L.rank + 1);
+  if (L.rg_hidden > 0) {
+    const RgArgs ra{Tp, U, ks, M, L.rank, rp1, L.rg_hidden, L.rg_W1, L.rg_b1, L.rg_W2, L.rg_b2,
+                    L.rg_alpha};
+    hipLaunchKernelGGL(prefill_rgate_kernel, dim3((M + kRgTok - 1) / kRgTok), dim3(256), 0, s, ra);
+    return hipGetLastError();
+  }
+  const UArgs ua{Tp, U, ks, M, L.rank, rp1, L.b_gate};
+  const int n = M * (rp1 / 4);
+  hipLaunchKernelGGL(prefill_u_kernel, dim3((n + 255) / 256), dim3(256), 0, s, ua);
+  return hipGetLastError();
+}
+
+// y = round(sum over ks splits of part [ks][M][N] (times the row's scale when
+// scale_rows) + U B^T when U is given), in 64 x 64 tiles.
+hipError_t launch_finish_parts(const LayerDesc &L, int dtype, uint16_t *y, int M, const float *part,
+                               int ks, const float *U, bool scale_rows, hipStream_t s) {
+  const UView uv = U ? UView{U, M, L.rank, rank_pad(L.rank + 1)} : UView{};
+  const FinishArgs fa{y, part, ks, L.scales, uv, L.B, L.N, M};
+  const dim3 fgrid((L.N + kFT - 1) / kFT, (M + kFT - 1) / kFT);
+  if (dtype == DT_F16)
+    launch_finish<DT_F16, true>(fa, fgrid, scale_rows, U != nullptr, s);
+  else
+    launch_finish<DT_BF16, true>(fa, fgrid, scale_rows, U != nullptr, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
                           void *ws, hipStream_t main_s, hipStream_t aux_s) {
   const bool ec = L.rank > 0;

@@ -1,0 +1,525 @@
+// Decode for 33..128 tokens ("wide" launch): y = dequant(W_q) x + g(x) B (A x),
+// still bound by the weight stream.
+//
+// The pages fuse the compensator into the memory-bound low-bit product and
+// keep a separate compensator kernel for the compute-bound phase (SPEAR
+// explanation page, Technical Summary 2.2 A).  Past 32 tokens a layer can
+// still be bound by its weight stream: Llama-70B's 8192 x 8192 at 64 tokens
+// needs 4.2 us of streaming at 8 TB/s for 3.4 us of dense fp16 MFMA work.
+// But with that many tokens the activation x (M K 2 bytes, 1 MiB at 64
+// tokens and K = 8192) must be reused across many output rows, which the
+// small-M decode kernels (16 to 64 rows per workgroup, each staging all of
+// x) do not do, and the K-splits that fill the chip need their partial sums
+// reduced.  Here the call is three stream-ordered launches, with no
+// workgroup ever waiting on another:
+//
+//  * wide_kernel: consumer workgroups of 8 waves own a tile of 128 R output
+//    rows (R 16-row blocks per wave) and one of ksp K-splits.  x for the
+//    split is streamed through LDS 512 columns at a time while each wave
+//    keeps the next four 128-wide blocks of its rows' packed nibbles in
+//    flight; each staged x fragment feeds R row blocks of 16x16x32 MFMAs and
+//    each dequantized weight word (exact, in registers) feeds every token
+//    block.  They store fp32 partial outputs [ksp][M][N] (or, at rank 0 with
+//    one split, round y directly).  Producer workgroups in the same launch
+//    store the K-split sums of [A; w_g] x for every token;
+//  * the compensator's U = g (A x) formed once from those sums, and
+//  * the finish kernel (both shared with the prefill path), which sums the
+//    partials in split order, adds U B^T and rounds y once.
+//
+// Every loop that touches memory has a compile-time shape, so its waits
+// count its loads exactly.
+#include <algorithm>
+#include <mutex>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace spear {
+
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCb = 4;               // 128-wide blocks per staged x chunk (= ring depth)
+constexpr int kChunkCols = 128 * kCb;
+constexpr int kXStr = kChunkCols + 8;  // LDS row stride of a staged chunk (halves)
+constexpr int kMaxLds = 160 * 1024;
+// Launch-shape constants of plan_wide (measured on MI355X).
+#ifndef SPEAR_WIDE_R64
+#define SPEAR_WIDE_R64 1  // 16-row blocks per wave at up to 64 tokens
+#endif
+#ifndef SPEAR_WIDE_WG_RATE
+#define SPEAR_WIDE_WG_RATE 25e9  // bytes/s of weights one workgroup streams
+#endif
+#ifndef SPEAR_WIDE_MAX_KSP
+#define SPEAR_WIDE_MAX_KSP 16
+#endif
+#ifndef SPEAR_WIDE_FORCE_KSP
+#define SPEAR_WIDE_FORCE_KSP 0  // > 0: that many K-splits (or the nearest count with no empty split)
+#endif
+
+struct WideArgs {
+  const uint32_t *qw;
+  const uint16_t *scales, *zeros;
+  const uint16_t *x;
+  uint16_t *y;
+  const uint16_t *A, *wg;
+  int N, K, G, ngroups, M, rank, rows;  // rows of [A; w_g]
+  int producers, ks, rp1;                // producers: row blocks of [A; w_g] x ks
+  int n_tiles, ksp, nbs, nb;             // tiles; K-splits; blocks per split; blocks of K
+  float *tp;        // [A; w_g] x sums [ks][M][rp1]
+  float *part;      // partial outputs [ksp][M][N] (null: y directly)
+  int buf_halves;   // halves of the staged x chunk (16 MB rows x kXStr)
+  int red_off;      // byte offset of the producers' wave sums in dynamic LDS
+};
+
+// Workgroup barrier for LDS only: this wave's LDS operations complete
+// (lgkmcnt(0)), then s_barrier.  __syncthreads() also carries a release fence
+// that waits for every outstanding global load (vmcnt(0)), which would drain
+// the weight and activation prefetches at every staged chunk.  The signal
+// fences keep the compiler from moving memory operations across.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// ---------------------------------------------------------------------------
+// Producers: one 16-row block of [A; w_g] over one K-split, for every token;
+// the sums go to tp[ksi][m][j].
+// ---------------------------------------------------------------------------
+template <int DT, int MB>
+__device__ void produce(const WideArgs &a, int p, f32x4_t *red, int tid) {
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 15, h = lane >> 4;
+  const int rb = p / a.ks, ksi = p % a.ks;
+  const int j = rb * 16 + col;
+  const bool jin = j < a.rows;
+  const uint16_t *arow = (j < a.rank) ? a.A + (size_t)j * a.K : (a.wg ? a.wg : a.A);
+  const int nsteps = a.K / 32;
+  const int per = (nsteps + a.ks - 1) / a.ks;
+  const int s0 = ksi * per, s1 = min(nsteps, s0 + per);
+  f32x4_t acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  for (int base = s0 + wave; base < s1; base += kWaves * 4) {
+    u32x4_t bo[4], ao[MB][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = min(base + kWaves * i, s1 - 1);
+      const int k = s * 32 + 8 * h;
+      bo[i] = *(const u32x4_t *)(arow + k);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = min(col + 16 * mb, a.M - 1);
+        ao[mb][i] = *(const u32x4_t *)(a.x + (size_t)m * a.K + k);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (base + kWaves * i < s1) {
+        const u32x4_t b = jin ? bo[i] : zero;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const u32x4_t av = (col + 16 * mb < a.M) ? ao[mb][i] : zero;
+          acc[mb] = mfma_16x16x32<DT>(av, b, acc[mb]);
+        }
+      }
+    }
+  }
+  // fixed-order sum over the waves (wave 0's own, then 1..7), one token block at a time
+  float *dst = a.tp + (size_t)ksi * a.M * a.rp1 + j;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    if (wave > 0) red[wave * 64 + lane] = acc[mb];
+    __syncthreads();
+    if (wave == 0) {
+      f32x4_t v = acc[mb];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) v = v + red[w * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * mb + 4 * h + e;
+        if (jin && m < a.M) dst[(size_t)m * a.rp1] = v[e];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Consumers.
+// ---------------------------------------------------------------------------
+template <int DT, int MB, int R, int D, bool PERCH>
+__device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 15, h = lane >> 4;
+  const int q = c % a.ksp, tile = c / a.ksp;
+  const int n0 = tile * 16 * R * kWaves;
+  int row[R];
+  const uint32_t *wrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    row[r] = min(n0 + 16 * (wave * R + r) + col, a.N - 1);
+    wrow[r] = a.qw + (size_t)row[r] * (a.K / 8);
+  }
+  const int kb0 = q * a.nbs;                 // the plan leaves no split empty
+  const int nbl = min(a.nb, kb0 + a.nbs) - kb0;
+  const int kx0 = kb0 * 128;
+  const int kend = min(a.K, kx0 + nbl * 128);  // staged columns past this are zeros
+
+  // per-channel: one zero-point constant and scale per row
+  uint32_t zc_row[R];
+  float s_row[R];
+  if constexpr (PERCH) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      zc_row[r] = zero_constant<DT>(a.zeros[row[r]]);
+      s_row[r] = (float)bitcast<_Float16>(a.scales[row[r]]);
+    }
+  }
+
+  // Groups of D blocks.  Group g's activation columns (kx0 + g D 128 ..) for
+  // every token are one staged chunk: loaded into registers (2 MB pieces of
+  // 16 bytes per thread) during group g - 1, stored to LDS between two
+  // barriers at the start of group g.  Every address is clamped into its
+  // array and every load is issued unconditionally, so a group is
+  // straight-line code whose waits count its loads exactly; columns past the
+  // split's end or past K are staged as zeros, which makes the padding blocks
+  // of the last group add exact zeros.
+  constexpr int kPieces = 2 * MB;  // (16 MB tokens x D 128 / 8 pieces) / 512 threads, D = 4
+  static_assert(D == 4, "one staged chunk per group of four blocks");
+  u32x4_t xr[kPieces];
+  auto xload = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int p = tid + kThreads * i;  // (token m, piece j): 64 pieces per token row
+      const int m = min(p >> 6, a.M - 1), j = p & 63;
+      const int k = min(kx0 + g * kChunkCols + 8 * j, a.K - 8);
+      xr[i] = *(const u32x4_t *)(a.x + (size_t)m * a.K + k);
+    }
+  };
+  // (the zero fill is a bit mask, so that the loop body stays one basic block)
+  auto xstore = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int p = tid + kThreads * i;
+      const int m = p >> 6, j = p & 63;
+      const uint32_t keep = (m < a.M && kx0 + g * kChunkCols + 8 * j < kend) ? ~0u : 0u;
+      const u32x4_t v = {xr[i][0] & keep, xr[i][1] & keep, xr[i][2] & keep, xr[i][3] & keep};
+      *(u32x4_t *)(lds + m * kXStr + 8 * j) = permute_8(v);
+    }
+  };
+
+  // the weight ring: block b of the split for row block r (clamped to the
+  // split's last block), with its group's scale and zero-point (group-wise)
+  // (scale and zero-point bits widened to 32-bit registers: two 16-bit values
+  // packed into one register would be loaded into its halves, each load then
+  // waiting for the other)
+  u32x4_t ring[D][R];
+  uint32_t sr[D][R], zr[D][R];
+  auto wload = [&](int b, int r, u32x4_t &w, uint32_t &sv, uint32_t &zv) {
+    const int kb = kb0 + min(b, nbl - 1);
+    const int off = (kb * 128 + 32 * h < a.K) ? kb * 16 + 4 * h : 0;
+    w = __builtin_nontemporal_load((const u32x4_t *)(wrow[r] + off));
+    if constexpr (!PERCH) {
+      const int g = (kb * 128) / a.G;
+      const size_t e = (size_t)row[r] * a.ngroups + g;
+      sv = (uint32_t)a.scales[e];
+      zv = (uint32_t)a.zeros[e];
+    }
+  };
+
+  // the same order of loads as each group issues them (activation chunk,
+  // then the ring), so that the waits at the top of the loop count the same
+  // loads whether the loop is entered or repeated
+  xload(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) wload(i, r, ring[i][r], sr[i][r], zr[i][r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  f32x4_t acc[R][MB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[r][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // A-operand rows past M read row M - 1 (their outputs are never stored)
+  int xrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) xrow[mb] = min(col + 16 * mb, a.M - 1) * kXStr;
+
+  // Each ring slot is dequantized before its refill is issued, so the refill
+  // can load into the slot's own registers: a slot still live when its
+  // refill issues would take a register copy at the loop's back edge, and
+  // that copy waits for the load, draining the ring every group.
+  const int ngr = (nbl + D - 1) / D;
+  for (int g = 0; g < ngr; ++g) {
+    lds_barrier();  // every wave is done with group g - 1's chunk
+    xstore(g);
+    lds_barrier();
+    xload(g + 1);     // clamped: past the split it reloads valid columns, staged as zeros
+    // keep the prefetches here: the scheduler would otherwise move loads whose
+    // results are only used by the next group down to just before that use
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int b = g * D + i;
+      u32x4_t bop[R][4];
+      float sc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        uint32_t zc;
+        if constexpr (PERCH) {
+          zc = zc_row[r];
+        } else {
+          zc = zero_constant<DT>((uint16_t)zr[i][r]);
+          sc[r] = (float)bitcast<_Float16>((uint16_t)sr[i][r]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bop[r][t] = dequant_word<DT>(ring[i][r][t], zc);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) wload(b + D, r, ring[i][r], sr[i][r], zr[i][r]);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t *xb = lds + i * 128 + 32 * h;
+      f32x4_t gacc[R][MB];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        u32x4_t xa[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) xa[mb] = *(const u32x4_t *)(xb + xrow[mb] + 8 * t);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            if constexpr (PERCH) {
+              acc[r][mb] = mfma_16x16x32<DT>(xa[mb], bop[r][t], acc[r][mb]);
+            } else {
+              gacc[r][mb] = mfma_16x16x32<DT>(xa[mb], bop[r][t],
+                                              t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : gacc[r][mb]);
+            }
+          }
+        }
+      }
+      if constexpr (!PERCH) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[r][mb] += sc[r] * gacc[r][mb];
+      }
+    }
+  }
+  if constexpr (PERCH) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[r][mb] *= s_row[r];
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = n0 + 16 * (wave * R + r) + col;
+    if (n < a.N) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 16 * mb + 4 * h + e;
+          if (m < a.M) {
+            if (a.part)
+              a.part[((size_t)q * a.M + m) * a.N + n] = acc[r][mb][e];
+            else
+              a.y[(size_t)m * a.N + n] = from_f32<DT>(acc[r][mb][e]);
+          }
+        }
+    }
+  }
+}
+
+// Workgroups per CU: two for the 64-token kernel with one row block per wave
+// (its registers and its 66 KB of staged x allow it), else one.
+template <int MB, int R>
+constexpr int wgs_per_cu() {
+  return (MB == 4 && R == 1) ? 2 : 1;
+}
+
+template <int DT, int MB, int R, int D, bool EC, bool PERCH>
+__global__ __launch_bounds__(kThreads, (wgs_per_cu<MB, R>())) void wide_kernel(WideArgs a) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  if constexpr (EC) {
+    if (b < a.producers) {
+      produce<DT, MB>(a, b, (f32x4_t *)((char *)lds + a.red_off), tid);
+      return;
+    }
+    consume<DT, MB, R, D, PERCH>(a, b - a.producers, lds, tid);
+  } else {
+    consume<DT, MB, R, D, PERCH>(a, b, lds, tid);
+  }
+}
+
+template <int DT, int MB, int R, bool EC, bool PERCH>
+hipError_t launch_t(const WideArgs &a, int grid, size_t lds, hipStream_t s) {
+  auto kern = wide_kernel<DT, MB, R, kCb, EC, PERCH>;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   kMaxLds);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int MB, int R>
+hipError_t launch_ec(const WideArgs &a, int grid, size_t lds, bool ec, bool perch, hipStream_t s) {
+  if (ec) return perch ? launch_t<DT, MB, R, true, true>(a, grid, lds, s)
+                       : launch_t<DT, MB, R, true, false>(a, grid, lds, s);
+  return perch ? launch_t<DT, MB, R, false, true>(a, grid, lds, s)
+               : launch_t<DT, MB, R, false, false>(a, grid, lds, s);
+}
+
+template <int DT>
+hipError_t launch_mb(const WideArgs &a, const WidePlan &p, bool ec, bool perch, hipStream_t s) {
+  const int grid = p.n_tiles * p.ksp + p.producers;
+  if (p.mb == 4) {
+    return p.r == 1 ? launch_ec<DT, 4, 1>(a, grid, p.lds, ec, perch, s)
+                    : launch_ec<DT, 4, 2>(a, grid, p.lds, ec, perch, s);
+  }
+  return launch_ec<DT, 8, 1>(a, grid, p.lds, ec, perch, s);  // 128 tokens: one row block per wave
+}
+
+// K-splits of the producers: about 2048 columns each, from 4 to 8.
+int wide_producer_ksplit(int K) {
+  const int need = (K / 32 + 63) / 64;
+  const int ks = (need + 3) / 4 * 4;
+  return ks < 4 ? 4 : (ks > 8 ? 8 : ks);
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+}  // namespace
+
+// Launch shape for M tokens (33..128): 16-token blocks MB (4 or 8), rows per
+// wave 16 R, and the K-split count ksp of the tiles of 128 R rows.  ksp is
+// the count whose estimated time is least, where too few workgroups leave
+// the weight stream short of loads in flight, and each split adds its fp32
+// partial outputs (M N 4 bytes) to write and for the finish kernel to read:
+//   time ~ max(weights / (resident workgroups x per-workgroup rate),
+//              (weights + partials) / HBM rate) + partials / re-read rate.
+WidePlan plan_wide(const LayerDesc &L, int M) {
+  WidePlan p{};
+  p.ok = false;
+  if (M < 1 || M > 128) return p;
+  p.mb = M <= 64 ? 4 : 8;
+  p.r = p.mb == 4 ? SPEAR_WIDE_R64 : 1;
+  p.rb_a = L.rank > 0 ? (L.rank + L.gate_rows() + 15) / 16 : 0;
+  p.ks = L.rank > 0 ? wide_producer_ksplit(L.K) : 0;
+  p.producers = p.rb_a * p.ks;
+  p.rp1 = (L.rank + 1 + 3) / 4 * 4;
+  p.nb = (L.K + 127) / 128;
+  const int tile_rows = 16 * p.r * kWaves;
+  p.n_tiles = (L.N + tile_rows - 1) / tile_rows;
+  const int resident = 256 * ((p.mb == 4 && p.r == 1) ? 2 : 1);
+  const double wbytes = (double)L.N * L.K / 2;
+  double best = 1e30;
+  for (int ks = 1; ks <= std::min(SPEAR_WIDE_MAX_KSP, p.nb); ++ks) {
+    const int nbs = (p.nb + ks - 1) / ks;
+    const int ksp = (p.nb + nbs - 1) / nbs;  // no empty split
+    if (ksp != ks) continue;
+    const int wgs = p.n_tiles * ksp;
+    const double live = std::min(wgs, resident);
+    const bool parts = ksp > 1 || L.rank > 0;
+    const double part = parts ? (double)ksp * L.N * M * 4 : 0.0;
+    double t = std::max(wbytes / (live * SPEAR_WIDE_WG_RATE), (wbytes + part) / 5e12) +
+               part / 8e12;
+    if (SPEAR_WIDE_FORCE_KSP > 0) t = std::abs(ksp - SPEAR_WIDE_FORCE_KSP);
+    if (t < best * 0.999) {
+      best = t;
+      p.ksp = ksp;
+      p.nbs = nbs;
+    }
+  }
+  p.direct = L.rank == 0 && p.ksp == 1;
+  p.buf_halves = 16 * p.mb * kXStr;
+  p.red_off = (int)round256((size_t)p.buf_halves * 2);
+  p.lds = p.red_off + (size_t)kWaves * 64 * 16;  // the producers' wave sums
+  p.tp_off = kWsDataOff;
+  p.u_off = p.tp_off + (L.rank > 0 ? round256((size_t)p.ks * M * p.rp1 * sizeof(float)) : 0);
+  p.part_off = p.u_off + (L.rank > 0 ? round256((size_t)M * p.rp1 * sizeof(float)) : 0);
+  p.end = p.direct ? 0 : p.part_off + round256((size_t)p.ksp * M * L.N * sizeof(float));
+  p.ok = p.lds <= (size_t)kMaxLds;
+  return p;
+}
+
+size_t wide_workspace_bytes(const LayerDesc &L, int M) {
+  const WidePlan p = plan_wide(L, M);
+  return p.ok ? p.end : 0;
+}
+
+int wide_launches(const LayerDesc &L, int M) {
+  const WidePlan p = plan_wide(L, M);
+  return p.direct ? 1 : (L.rank > 0 ? 3 : 2);
+}
+
+void describe_wide(const LayerDesc &L, int M, spear_plan_t *out) {
+  const WidePlan p = plan_wide(L, M);
+  out->path = SPEAR_PATH_DECODE_WIDE;
+  out->workgroups = p.n_tiles * p.ksp + p.producers;
+  out->waves_per_workgroup = kWaves;
+  out->producers = p.producers;
+  out->k_splits = p.ksp;
+  out->workspace_bytes = p.end;
+}
+
+hipError_t launch_wide(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
+                       void *ws, hipStream_t s) {
+  const WidePlan p = plan_wide(L, M);
+  if (!p.ok || (!p.direct && !ws)) return hipErrorInvalidConfiguration;
+  char *base = (char *)ws;
+  WideArgs a{};
+  a.qw = L.qw;
+  a.scales = L.scales;
+  a.zeros = L.zeros;
+  a.x = x;
+  a.y = y;
+  a.A = L.A;
+  a.wg = L.wg;
+  a.N = L.N;
+  a.K = L.K;
+  a.G = L.G;
+  a.ngroups = L.ngroups;
+  a.M = M;
+  a.rank = L.rank;
+  a.rows = L.rank + L.gate_rows();
+  a.producers = p.producers;
+  a.ks = p.ks;
+  a.rp1 = p.rp1;
+  a.n_tiles = p.n_tiles;
+  a.ksp = p.ksp;
+  a.nbs = p.nbs;
+  a.nb = p.nb;
+  a.tp = L.rank > 0 ? (float *)(base + p.tp_off) : nullptr;
+  a.part = p.direct ? nullptr : (float *)(base + p.part_off);
+  a.buf_halves = p.buf_halves;
+  a.red_off = p.red_off;
+  const bool ec = L.rank > 0;
+  hipError_t e = dtype == DT_F16 ? launch_mb<DT_F16>(a, p, ec, L.per_channel, s)
+                                 : launch_mb<DT_BF16>(a, p, ec, L.per_channel, s);
+  if (e != hipSuccess || p.direct) return e;
+  float *U = nullptr;
+  if (ec) {
+    U = (float *)(base + p.u_off);
+    if ((e = launch_form_u(L, a.tp, p.ks, M, U, s)) != hipSuccess) return e;
+  }
+  // the scale is already applied to the partials (per-channel: at the end of the main loop)
+  return launch_finish_parts(L, dtype, y, M, a.part, p.ksp, U, false, s);
+}
+
+}  // namespace spear

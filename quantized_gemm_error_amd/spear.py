@@ -23,7 +23,7 @@ SPEAR_ERR_HIP = 4
 SPEAR_F16 = 0
 SPEAR_BF16 = 1
 SPEAR_MAX_RANK = 128
-SPEAR_MAX_DECODE_M = 32
+SPEAR_MAX_DECODE_M = 128
 
 # Every function the header declares, for the export check.
 EXPORTED = (
@@ -42,7 +42,8 @@ SPEAR_PATH_NONE = 0
 SPEAR_PATH_DECODE = 1
 SPEAR_PATH_DECODE_SPLIT = 2
 SPEAR_PATH_PREFILL = 3
-PATH_NAMES = {0: "none", 1: "decode", 2: "decode_split", 3: "prefill"}
+SPEAR_PATH_DECODE_WIDE = 4
+PATH_NAMES = {0: "none", 1: "decode", 2: "decode_split", 3: "prefill", 4: "decode_wide"}
 
 
 class SpearError(RuntimeError):

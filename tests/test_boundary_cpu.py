@@ -68,15 +68,17 @@ def test_select_chunk_invalid(lib):
 
 
 def test_decode_max_m_setting(lib):
-    assert spear.spear_get_decode_max_m() == 32
+    assert spear.spear_get_decode_max_m() == 64
     spear.spear_set_decode_max_m(16)
     assert spear.spear_get_decode_max_m() == 16
-    spear.spear_set_decode_max_m(32)
+    spear.spear_set_decode_max_m(128)
+    assert spear.spear_get_decode_max_m() == 128
+    spear.spear_set_decode_max_m(64)
     with pytest.raises(spear.SpearError):
         spear.spear_set_decode_max_m(0)
     with pytest.raises(spear.SpearError):
-        spear.spear_set_decode_max_m(33)
-    assert spear.spear_get_decode_max_m() == 32
+        spear.spear_set_decode_max_m(129)
+    assert spear.spear_get_decode_max_m() == 64
 
 
 def test_decode_split_min_m_setting(lib):
@@ -162,7 +164,7 @@ def test_rejects_bad_io_and_workspace(lib):
     assert _decode(lib, lay, x=None) == 1
     assert _decode(lib, lay, x=FAKE * 2 + 8) == 1          # x not 16-byte aligned
     assert _decode(lib, lay, y=FAKE * 2) == 1              # y aliases x
-    assert _decode(lib, lay, M=33) == 1
+    assert _decode(lib, lay, M=129) == 1
     assert _decode(lib, lay, M=-1) == 1
     assert _decode(lib, lay, ws=None) == 3
     assert _decode(lib, lay, ws_bytes=16) == 3
@@ -245,13 +247,17 @@ def test_plan_dispatch_and_errors(lib):
     assert _plan(lay, 0, ws)["path"] == "none"
     assert _plan(lay, 1, ws)["path"] == "decode"
     assert _plan(lay, 32, ws)["path"] == "decode"
-    assert _plan(lay, 33, ws)["path"] == "prefill"
+    assert _plan(lay, 33, ws)["path"] == "decode_wide"
+    assert _plan(lay, 64, ws)["path"] == "decode_wide"
+    assert _plan(lay, 65, ws)["path"] == "prefill"
     assert _plan(lay, 2048, ws)["path"] == "prefill"
     assert _plan(lay, 2048, ws)["k_splits"] == 1
-    assert _plan(lay, 64, ws)["k_splits"] > 1          # 32 output tiles: K split
+    assert _plan(lay, 64, ws, "prefill")["k_splits"] > 1   # 32 output tiles: K split
     assert _plan(lay, 16, ws, "prefill")["path"] == "prefill"
+    assert _plan(lay, 33, ws, "decode")["path"] == "decode_wide"
+    assert _plan(lay, 128, ws, "decode")["path"] == "decode_wide"
     with pytest.raises(spear.SpearError):
-        _plan(lay, 33, ws, "decode")
+        _plan(lay, 129, ws, "decode")
     with pytest.raises(spear.SpearError):               # compensated: workspace required
         _plan(lay, 1, 0)
     with pytest.raises(spear.SpearError):
@@ -289,3 +295,28 @@ def test_graph_calls_reject_null_handles(lib):
     assert lib.spear_graph_end(None) == 1
     assert lib.spear_graph_launch(None, None) == 1
     assert lib.spear_graph_destroy(None) == 0
+
+
+@pytest.mark.parametrize("K,N,G,r", [(8192, 8192, 8192, 64), (8192, 28672, 8192, 64),
+                                     (28672, 8192, 28672, 64), (4096, 4096, 128, 32),
+                                     (11008, 4096, 128, 32), (512, 512, 512, 16), (640, 300, 128, 24)])
+def test_wide_decode_plans(lib, K, N, G, r):
+    """33..128 tokens plan the wide decode launch: tiles of 128 or 256 rows times K-splits
+    (never an empty split) plus the compensator's producers, and a workspace that the call
+    accepts; a compensated call needs one."""
+    lay = _layer(N=N, K=K, group_size=G, rank=r)
+    ws = lib.spear_workspace_bytes(ctypes.byref(lay), 128)
+    for M in (33, 48, 64, 65, 100, 128):
+        p = _plan(lay, M, ws, "decode")
+        assert p["path"] == "decode_wide"
+        nb = -(-K // 128)
+        assert 1 <= p["k_splits"] <= nb
+        nbs = -(-nb // p["k_splits"])
+        assert -(-nb // nbs) == p["k_splits"]          # no empty split
+        consumers = p["workgroups"] - p["producers"]
+        assert consumers % p["k_splits"] == 0
+        assert consumers // p["k_splits"] in (-(-N // 128), -(-N // 256))
+        assert p["workspace_bytes"] <= ws
+        assert _plan(lay, M, p["workspace_bytes"], "decode")["path"] == "decode_wide"
+        with pytest.raises(spear.SpearError):       # compensated: the workspace is required
+            _plan(lay, M, 0, "decode")

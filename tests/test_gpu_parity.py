@@ -194,6 +194,74 @@ def test_decode_wait_expiry_computes_the_sums_itself(N, K, G, r, M, dtype, split
     assert hdr[0] == 0 and hdr[2:] == [0] * 10   # counters reset; only the flags word is set
 
 
+# The wide decode launch (33..128 tokens): 256-row tiles (128 rows past 64 tokens) over
+# K-splits, x streamed through LDS in 256-column chunks.
+WIDE_CASES = [
+    # N, K, G, r, M, dtype, outliers, hidden (per-rank gate; 0: scalar gate)
+    (512, 512, 0, 16, 64, "f16", False, 0),       # the small layer at 64 tokens
+    (300, 1024, 128, 32, 33, "f16", True, 0),     # ragged tile (300 rows), 33 tokens
+    (1024, 4096, 128, 32, 48, "bf16", True, 0),   # bf16, several K-splits
+    (640, 2176, 0, 24, 64, "f16", True, 0),       # per-channel, K % 256 != 0 (odd block count)
+    (256, 2080, 0, 8, 100, "bf16", False, 0),     # K % 128 != 0: a partial last block
+    (520, 1536, 128, 128, 128, "f16", True, 0),   # the largest rank at 128 tokens
+    (384, 1024, 256, 40, 65, "f16", True, 0),     # G = 256, 65 tokens (128-token kernel)
+    (256, 4096, 128, 0, 64, "f16", True, 0),      # rank 0
+    (96, 512, 128, 40, 64, "f16", True, 64),      # per-rank gate, widest hidden layer
+    (300, 2048, 0, 24, 90, "bf16", True, 8),      # per-rank gate, 128-token kernel
+    (33000, 256, 128, 16, 40, "f16", False, 0),   # 129 tiles: more than the tile counters, no K split
+]
+
+
+@pytest.mark.parametrize("N,K,G,r,M,dtype,outl,hidden", WIDE_CASES)
+def test_decode_wide_parity(N, K, G, r, M, dtype, outl, hidden):
+    note(f"decode wide N={N} K={K} G={G} r={r} M={M} {dtype} hidden={hidden}")
+    hl, xb, lay, x = _setup(N, K, G, r, seed=N + K + r + M, dtype=dtype, M=M, outliers=outl,
+                            b_gate=0.15)
+    params = None
+    if hidden:
+        params = synth.make_rank_gate(r, hidden, seed=N + r, t_scale=0.01 * np.sqrt(K))
+        lay.rank_gate = spear.rank_gate_to_device(params, 1.1, DEV)
+    ws = spear.new_workspace(lay, M)
+    plan = spear.spear_linear_plan(lay, M, ws.numel(), "decode")
+    note(f"  plan {plan}")
+    assert plan["path"] == "decode_wide"
+    y = spear.spear_linear_decode(lay, x, workspace=ws)
+    torch.cuda.synchronize()
+    ref = _rank_gate_ref(hl, xb, params, 1.1) if hidden else oracle_y(hl, xb)
+    assert_close(gpu_y_f64(y, dtype), ref, f"decode wide {N}x{K} M={M}")
+    assert spear.spear_workspace_flags(ws) == 0
+    assert _ws_header(ws) == [0] * 12
+
+
+@pytest.mark.parametrize("M", [48, 100])
+def test_decode_wide_never_waits(M):
+    """The wide launch has no wait between workgroups (its compensator and split sums are
+    joined by kernel boundaries): with the poll limit at 0 it still matches the oracle and
+    sets no flag."""
+    note(f"decode wide, poll limit 0, M={M}")
+    hl, xb, lay, x = _setup(700, 2048, 128, 32, seed=M + 3, M=M, outliers=True, b_gate=0.3)
+    with decode_spin_limit(0):
+        ws = spear.new_workspace(lay, M)
+        y = spear.spear_linear_decode(lay, x, workspace=ws)
+        torch.cuda.synchronize()
+    assert_close(gpu_y_f64(y, "f16"), oracle_y(hl, xb), "wide, poll limit 0")
+    assert spear.spear_workspace_flags(ws) == 0
+    assert _ws_header(ws) == [0] * 12
+
+
+def test_decode_wide_gate_off_is_rank_zero_bitwise():
+    note("wide gate off")
+    hl, xb, lay, x = _setup(512, 2048, 128, 32, seed=6, M=64, outliers=True)
+    lay.w_gate = torch.zeros_like(lay.w_gate)
+    lay.b_gate = float("-inf")
+    ws = spear.new_workspace(lay, 64)
+    y_off = spear.spear_linear_decode(lay, x, workspace=ws)
+    lay0 = lay.without_compensator()
+    y_r0 = spear.spear_linear_decode(lay0, x, workspace=spear.new_workspace(lay0, 64))
+    torch.cuda.synchronize()
+    assert torch.equal(y_off.view(torch.int16), y_r0.view(torch.int16))
+
+
 @pytest.mark.parametrize("M", [1, 4, 16, 32])
 def test_decode_gate_off_is_rank_zero_bitwise(M):
     note(f"gate off M={M}")
@@ -547,21 +615,29 @@ def test_prefill_gate_off_matches_rank_zero():
 
 
 def test_decode_and_prefill_agree_and_dispatch():
+    """spear_linear: up to 64 tokens (the default threshold) the decode launches, past it the
+    prefill path; every path matches the oracle and the dispatched calls are bitwise the
+    explicit ones."""
     note("dispatch")
-    hl, xb, lay, x = _setup(200, 1024, 128, 32, seed=12, M=48, outliers=True)
-    ws = spear.new_workspace(lay, 48)
+    hl, xb, lay, x = _setup(200, 1024, 128, 32, seed=12, M=80, outliers=True)
+    ws = spear.new_workspace(lay, 80)
     ref = oracle_y(hl, xb)
-    x32 = x[:32].contiguous()
+    x32, x48 = x[:32].contiguous(), x[:48].contiguous()
     yd = spear.spear_linear_decode(lay, x32, workspace=ws)
     yp = spear.spear_linear_prefill(lay, x32, workspace=ws)
     yl32 = spear.spear_linear(lay, x32, workspace=ws)
-    yl48 = spear.spear_linear(lay, x, workspace=ws)
-    yp48 = spear.spear_linear_prefill(lay, x, workspace=ws)
+    yw48 = spear.spear_linear_decode(lay, x48, workspace=ws)
+    yl48 = spear.spear_linear(lay, x48, workspace=ws)
+    yl80 = spear.spear_linear(lay, x, workspace=ws)
+    yp80 = spear.spear_linear_prefill(lay, x, workspace=ws)
     torch.cuda.synchronize()
     assert_close(gpu_y_f64(yd, "f16"), ref[:32], "decode")
     assert_close(gpu_y_f64(yp, "f16"), ref[:32], "prefill")
+    assert_close(gpu_y_f64(yw48, "f16"), ref[:48], "decode wide")
+    assert_close(gpu_y_f64(yp80, "f16"), ref, "prefill 80")
     assert torch.equal(yl32.view(torch.int16), yd.view(torch.int16))     # M = 32 -> decode
-    assert torch.equal(yl48.view(torch.int16), yp48.view(torch.int16))   # M = 48 -> prefill
+    assert torch.equal(yl48.view(torch.int16), yw48.view(torch.int16))   # M = 48 -> decode (wide)
+    assert torch.equal(yl80.view(torch.int16), yp80.view(torch.int16))   # M = 80 -> prefill
 
 
 def test_prefill_rank0_split_k_with_and_without_workspace():
@@ -678,11 +754,20 @@ def test_llama70b_layer_sampled(K, N):
         x = spear.act_to_device(xb, "f16", DEV)
         ws = spear.new_workspace(lay, M)
         ref = oracle_y(hl, xb, rows=rows)
+        if 32 < M <= spear.SPEAR_MAX_DECODE_M:   # the wide decode launch, asked for explicitly
+            note(f"llama70b K={K} N={N} M={M} decode_wide")
+            y = spear.spear_linear_decode(lay, x, workspace=ws)
+            torch.cuda.synchronize()
+            assert_close(gpu_y_f64(y, "f16")[:, rows], ref, f"70B {K}->{N} M={M} wide")
+            assert spear.spear_workspace_flags(ws) == 0
+            assert _ws_header(ws) == [0] * 12
         for schedule in (("serial",) if M <= 32 else ("serial", "concurrent")):
             note(f"llama70b K={K} N={N} M={M} {schedule} "
                  f"{spear.spear_linear_plan(lay, M, ws.numel())['path']}")
             aux = torch.cuda.Stream() if schedule == "concurrent" else None
-            y = spear.spear_linear(lay, x, workspace=ws, aux_stream=aux)
+            # up to 32 tokens the dispatch (decode); past that the prefill path explicitly
+            call = spear.spear_linear if M <= 32 else spear.spear_linear_prefill
+            y = call(lay, x, workspace=ws, aux_stream=aux)
             torch.cuda.synchronize()
             assert_close(gpu_y_f64(y, "f16")[:, rows], ref, f"70B {K}->{N} M={M} {schedule}")
             assert spear.spear_workspace_flags(ws) == 0

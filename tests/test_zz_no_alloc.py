@@ -54,8 +54,8 @@ def test_noalloc_matches_workspace_entry_point(N, K, G, r, Ms, dtype):
 def test_noalloc_rejects_bad_arguments():
     hl = synth.make_layer(256, 512, 128, 8, seed=3)
     lay = spear.layer_to_device(hl, DEV)
-    x = spear.act_to_device(synth.make_activations(33, 512, seed=3), "f16", DEV)
+    x = spear.act_to_device(synth.make_activations(129, 512, seed=3), "f16", DEV)
     with pytest.raises(spear.SpearError):
-        spear.spear_linear_decode_noalloc(lay, x)          # 33 tokens: beyond decode
+        spear.spear_linear_decode_noalloc(lay, x)          # 129 tokens: beyond decode
     y = spear.spear_linear_decode_noalloc(lay, x[:0])     # M = 0: a no-op
     assert y.shape == (0, 256)
