@@ -356,9 +356,10 @@ def random_layer(torch, N, K, G, r, device, gen, act):
     """A 4-bit layer drawn directly on the device, for timing only (values do not change
     the work): random packed codes, fp16 scales in [0.001, 0.005), integer zero-points,
     A, B ~ N(0, 0.01), w_g ~ N(0, 0.05)."""
-    from quantized_gemm_error_amd.spear import SpearLayer
+    from quantized_gemm_error_amd.spear import SpearLayer, qweight_rows
     ng = K // G
-    qw = torch.randint(-2**31, 2**31 - 1, (N, K // 8), dtype=torch.int32, device=device, generator=gen)
+    qw = torch.randint(-2**31, 2**31 - 1, (qweight_rows(N), K // 8), dtype=torch.int32,
+                       device=device, generator=gen)
     sc = (torch.rand((N, ng), device=device, generator=gen) * 0.004 + 0.001).to(torch.float16)
     zp = torch.randint(0, 16, (N, ng), device=device, generator=gen).to(torch.float16)
     lay = SpearLayer(N=N, K=K, group_size=G, qweight=qw, scales=sc, zeros=zp, rank=r)

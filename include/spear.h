@@ -71,9 +71,18 @@ typedef void *spear_stream_t; /* a hipStream_t */
  *   group_size  G: columns per scale/zero-point group.  G == K means one
  *               group per output row (per-channel).  Otherwise G % 128 == 0
  *               and K % G == 0.
- *   qweight     int32 [N][K/8], 16-byte aligned.  Code k = 8j+i of row n is
- *               bits 4i..4i+3 of word j of that row (lowest nibble first),
- *               unsigned 0..15.  spear_pack_int4 produces this layout.
+ *   qweight     int32, SPEAR_QWEIGHT_WORDS(N, K) words, 16-byte aligned, in
+ *               the tiled order.  Eight unsigned codes (0..15) per word along
+ *               K, lowest nibble first: code k = 8j+i of row n is bits
+ *               4i..4i+3 of that row's word j.  The words are stored by
+ *               blocks of 16 rows (N padded with zero words to a multiple of
+ *               16): inside a block, piece P (words 4P..4P+3, codes
+ *               32P..32P+31) of rows 0..15, then piece P+1 of rows 0..15, and
+ *               so on.  Word j of row n is thus at word index
+ *                 (n / 16) * 2K + (j / 4) * 64 + (n % 16) * 4 + j % 4,
+ *               and each 128-code tile of a row block is 1 KB in the order a
+ *               64-lane wave loads it.  spear_pack_int4 (from codes) and
+ *               spear_tile_int4 (from row-after-row words) produce it.
  *   scales      fp16 bit patterns [N][K/G], row-major (16-byte alignment is
  *               not required, but it is the fast path).
  *   zeros       fp16 bit patterns [N][K/G]: the zero-point as a code value
@@ -149,13 +158,28 @@ typedef struct spear_layer {
  */
 size_t spear_workspace_bytes(const spear_layer_t *layer, int32_t M);
 
+/* Words of qweight for an N x K layer: rows padded to a multiple of 16. */
+#define SPEAR_QWEIGHT_WORDS(N, K) ((((int64_t)(N) + 15) / 16) * 16 * ((int64_t)(K) / 8))
+
 /*
- * Pack 4-bit codes: q uint8 [N][K] (device; only the low 4 bits of each byte
- * are used) -> qweight int32 [N][K/8] (device, 16-byte aligned) in the
- * layout described at spear_layer_t.  K % 8 == 0.  Bit-exact.
+ * Pack 4-bit codes (the pages' 4-bit weight, Problem Statement and 2.1 A):
+ * q uint8 [N][K] (device, row-major; only the low 4 bits of each byte are
+ * used) -> qweight, SPEAR_QWEIGHT_WORDS(N, K) int32 words (device, 16-byte
+ * aligned, written in full including the zero padding rows) in the tiled
+ * order described at spear_layer_t.  K % 32 == 0.  Bit-exact.
  * Not a step of the layer itself: the packing done once per layer.
+ * Asynchronous on stream; the caller owns both buffers.
  */
 spear_status_t spear_pack_int4(const uint8_t *q, int32_t *qweight, int64_t N, int64_t K,
+                               spear_stream_t stream);
+
+/*
+ * Reorder words packed row after row (int32 [N][K/8], the same eight codes
+ * per word, lowest nibble first, 16-byte aligned) into the tiled order:
+ * qweight as for spear_pack_int4.  For loading weights that were packed
+ * elsewhere.  K % 32 == 0; the two buffers must not overlap.  Bit-exact.
+ */
+spear_status_t spear_tile_int4(const int32_t *words, int32_t *qweight, int64_t N, int64_t K,
                                spear_stream_t stream);
 
 /*

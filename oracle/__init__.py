@@ -13,6 +13,8 @@ Every function pins to something other than itself in ``tests/test_oracle.py``
 values).  Parity status per function:
 
 * ``unpack_int4`` / ``pack_int4``  - pinned (exhaustive, hand word, round trip)
+* ``tile_words`` / ``untile_words`` - pinned (per-code byte addresses, hand
+                                     tile, padding, round trip)
 * ``dequant``                      - pinned (brute force, integer closed form)
 * ``sigmoid`` / ``gate``           - pinned (special values, symmetry, math.exp)
 * ``spear_linear_ref``             - pinned (brute force, r=0, gate off/on,
@@ -35,5 +37,7 @@ from .spear_ref import (  # noqa: F401
     select_chunk_ref,
     sigmoid,
     spear_linear_ref,
+    tile_words,
     unpack_int4,
+    untile_words,
 )

@@ -107,6 +107,36 @@ def pack_int4(q) -> np.ndarray:
     return words.view(np.int32)
 
 
+def tile_words(qweight) -> np.ndarray:
+    """Row-major packed words [N][K/8] -> the GPU library's tiled order.
+
+    A layout, not arithmetic: the pages fix 4-bit codes packed eight to a
+    32-bit word and leave the order of the words in memory open.  The rows
+    are padded with zero words to a multiple of 16 and taken in blocks of 16
+    rows; inside a block, piece P (words 4P .. 4P + 3, codes 32P .. 32P + 31)
+    of rows 0..15 comes first, then piece P + 1 of rows 0..15, and so on.
+    The result is returned as int32 [ceil(N/16) 16][K/8], whose row index no
+    longer names an output row.
+    """
+    words = np.ascontiguousarray(np.asarray(qweight, dtype=np.int32))
+    n_rows, n_words = words.shape
+    if n_words % 4 != 0:
+        raise ValueError("K must be a multiple of 32 for the tiled order")
+    n_pad = -(-n_rows // 16) * 16
+    padded = np.zeros((n_pad, n_words), dtype=np.int32)
+    padded[:n_rows] = words
+    pieces = padded.reshape(n_pad // 16, 16, n_words // 4, 4)     # [block][row][piece][word]
+    return np.ascontiguousarray(pieces.transpose(0, 2, 1, 3)).reshape(n_pad, n_words)
+
+
+def untile_words(tiled, n_rows: int) -> np.ndarray:
+    """The inverse of ``tile_words``: the first n_rows row-major rows."""
+    t = np.ascontiguousarray(np.asarray(tiled, dtype=np.int32))
+    n_pad, n_words = t.shape
+    pieces = t.reshape(n_pad // 16, n_words // 4, 16, 4)          # [block][piece][row][word]
+    return np.ascontiguousarray(pieces.transpose(0, 2, 1, 3)).reshape(n_pad, n_words)[:n_rows]
+
+
 # ---------------------------------------------------------------------------
 # Dequantization: W = dequant(W_q) (pages: the compensator repairs the error
 # of the 4-bit weight; Problem Statement and 2.1 A)

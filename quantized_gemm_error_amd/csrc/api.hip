@@ -215,11 +215,28 @@ size_t spear_workspace_bytes(const spear_layer_t *layer, int32_t M) {
 spear_status_t spear_pack_int4(const uint8_t *q, int32_t *qweight, int64_t N, int64_t K,
                                spear_stream_t stream) {
   if (N < 0 || K < 0) return fail(SPEAR_ERR_INVALID_ARGUMENT, "N and K must be >= 0");
-  if (K % 8 != 0) return fail(SPEAR_ERR_INVALID_ARGUMENT, "K=%lld is not a multiple of 8", (long long)K);
+  if (K % 32 != 0)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "K=%lld is not a multiple of 32", (long long)K);
   if (N == 0 || K == 0) return ok();
   if (!q || !qweight) return fail(SPEAR_ERR_INVALID_ARGUMENT, "q and qweight must not be NULL");
-  if (!aligned(qweight, 4)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "qweight not 4-byte aligned");
+  if (!aligned(qweight, 16)) return fail(SPEAR_ERR_INVALID_ARGUMENT, "qweight not 16-byte aligned");
   return hip_status(launch_pack_int4(q, qweight, N, K, (hipStream_t)stream), "pack launch");
+}
+
+spear_status_t spear_tile_int4(const int32_t *words, int32_t *qweight, int64_t N, int64_t K,
+                               spear_stream_t stream) {
+  if (N < 0 || K < 0) return fail(SPEAR_ERR_INVALID_ARGUMENT, "N and K must be >= 0");
+  if (K % 32 != 0)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "K=%lld is not a multiple of 32", (long long)K);
+  if (N == 0 || K == 0) return ok();
+  if (!words || !qweight) return fail(SPEAR_ERR_INVALID_ARGUMENT, "words and qweight must not be NULL");
+  if (!aligned(words, 16) || !aligned(qweight, 16))
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "words and qweight must be 16-byte aligned");
+  const uintptr_t w0 = (uintptr_t)words, w1 = w0 + (uintptr_t)(N * (K / 2));
+  const uintptr_t q0 = (uintptr_t)qweight, q1 = q0 + (uintptr_t)((N + 15) / 16 * 8 * K);
+  if (w0 < q1 && q0 < w1)
+    return fail(SPEAR_ERR_INVALID_ARGUMENT, "words and qweight overlap (not an in-place call)");
+  return hip_status(launch_tile_int4(words, qweight, N, K, (hipStream_t)stream), "tile launch");
 }
 
 spear_status_t spear_linear_decode(const spear_layer_t *layer, spear_dtype_t dtype, const void *x,

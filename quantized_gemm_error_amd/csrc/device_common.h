@@ -43,6 +43,22 @@ __device__ __forceinline__ f32x4_t mfma_16x16x4_f32(float a, float b, f32x4_t c)
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// The packed weight's tiled order: rows in blocks of 16 (row count padded to
+// a multiple of 16), each block 2 K words long, made of 1 KB tiles of 128
+// codes in which lane 16 h + r of a wave finds, at word 4 (16 h + r), the
+// four words of row r that hold the tile's codes 32 h .. 32 h + 31.
+// tiled_block gives that lane's piece in tile 0 of the block holding row
+// n_block (a multiple of 16; past the last row the last block, so that every
+// address stays inside the array); tile kb is 256 kb words further on.  A
+// piece that would start past K (a partial last tile, or K < 128) must be
+// read from 4 lane words back, the block's first piece, which is always
+// inside the array.
+__device__ __forceinline__ const uint32_t *tiled_block(const uint32_t *qw, int n_block, int N,
+                                                       int K, int lane) {
+  const int rb = min(n_block, N - 1) >> 4;
+  return qw + (size_t)rb * 2 * K + 4 * lane;
+}
+
 // Per-row zero-point constant for dequant_word.
 //   fp16: packed pair of -(1024 + z) (exact: 1024 + z is an integer < 2048).
 //   bf16: 2^23 + z as an fp32 bit pattern.

@@ -134,6 +134,8 @@ hipError_t launch_finish_parts(const LayerDesc &L, int dtype, uint16_t *y, int M
                                int ks, const float *U, bool scale_rows, hipStream_t s);
 
 hipError_t launch_pack_int4(const uint8_t *q, int32_t *out, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_tile_int4(const int32_t *words, int32_t *out, int64_t N, int64_t K,
+                            hipStream_t s);
 hipError_t launch_decode(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
                          void *ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,

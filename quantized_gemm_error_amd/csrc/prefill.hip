@@ -151,6 +151,12 @@ __device__ __forceinline__ void gemm_tile(int &tm, int &tn) {
   tn = r / gsz;
 }
 
+// Weight piece p (0 .. 511) of a BN-row tile's k-block: lane p & 63 of the
+// tile's 16-row block p >> 6, i.e. tile row 16 (p >> 6) + (p & 15) and
+// codes 32 q .. 32 q + 31 of the block for q = (p & 63) >> 4.
+__device__ __forceinline__ int wpiece_row(int p) { return 16 * (p >> 6) + (p & 15); }
+__device__ __forceinline__ int wpiece_quarter(int p) { return (p & 63) >> 4; }
+
 template <int DT, bool PERCH, bool EPI, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
   static_assert(!(EPI && SPLIT), "split tiles are finished by prefill_finish_kernel");
@@ -177,11 +183,14 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
   // offset is loop-invariant, and the k-block's advance goes into the
   // scalar offset.  The scalar offset is not range-checked, so a k-block
   // that runs past K (K % 128 != 0) takes the guarded loads instead.
+  // (the packed weight's rows are padded to a multiple of 16 in memory; the
+  // padding is part of the tiled order, so the weight resource covers it)
   const int mrows = min(BM, a.M - m0), nrows = min(BN, a.N - n0);
+  const int nrows_p = min(BN, ((a.N + 15) & ~15) - n0);
   const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.x + (size_t)m0 * a.K), (short)0, mrows * a.K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.qw + (size_t)n0 * kw), (short)0, nrows * kw * 4, 0x00020000);
+      (void *)(a.qw + (size_t)n0 * kw), (short)0, nrows_p * kw * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t z_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.zeros + (size_t)n0 * a.ngroups), (short)0, nrows * a.ngroups * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -192,11 +201,14 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
     const int p = tid + 256 * i;
     x_off[i] = ((p >> 4) * a.K + 8 * (p & 15)) * 2;
   }
+  // weight piece i of this thread: lane p & 63 of 16-row block p >> 6 in the
+  // tiled order (row 16 (p >> 6) + (p & 15), codes 32 ((p & 63) >> 4) .. of
+  // each 128-code tile); the k-block's advance is 1 KB per tile
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = tid + 256 * i;
-    w_off[i] = ((p >> 2) * kw + 4 * (p & 3)) * 4;
-    z_off[i] = (p >> 2) * a.ngroups * 2;
+    w_off[i] = ((p >> 6) * 2 * a.K + 4 * (p & 63)) * 4;
+    z_off[i] = wpiece_row(p) * a.ngroups * 2;
   }
   const int s_off = tid * a.ngroups * 2;
 
@@ -213,10 +225,11 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int p = tid + 256 * i;
-      const int r = p >> 2, q4 = p & 3;
+      const int r = wpiece_row(p), q4 = wpiece_quarter(p);
       const int n = min(n0 + r, a.N - 1);
       const int k = kb * BK + 32 * q4;
-      wr[i] = (k < a.K) ? *(const u32x4_t *)(a.qw + (size_t)n * kw + kb * 16 + 4 * q4)
+      wr[i] = (k < a.K) ? *(const u32x4_t *)(tiled_block(a.qw, n0 + 16 * (p >> 6), a.N, a.K,
+                                                         p & 63) + kb * 256)
                         : u32x4_t{0u, 0u, 0u, 0u};
       zr[i] = a.zeros[(size_t)n * a.ngroups + g];
     }
@@ -233,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
     const int g = PERCH ? 0 : min((kb * BK) / a.G, a.ngroups - 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      wr[i] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off[i], kb * 64, 0);
+      wr[i] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, w_off[i], kb * 1024, 0);
       zr[i] = __builtin_amdgcn_raw_buffer_load_b16(z_rs, z_off[i], g * 2, 0);
     }
     if (!PERCH && tid < BN) sv = __builtin_amdgcn_raw_buffer_load_b16(s_rs, s_off, g * 2, 0);
@@ -251,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int p = tid + 256 * i;
-      const int r = p >> 2, q4 = p & 3;
+      const int r = wpiece_row(p), q4 = wpiece_quarter(p);
       const uint32_t zc = zero_constant<DT>(zr[i]);
 #pragma unroll
       for (int t = 0; t < 4; ++t)

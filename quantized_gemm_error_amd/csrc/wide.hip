@@ -158,11 +158,11 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   const int q = c % a.ksp, tile = c / a.ksp;
   const int n0 = tile * 16 * R * kWaves;
   int row[R];
-  const uint32_t *wrow[R];
+  const uint32_t *wblk[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     row[r] = min(n0 + 16 * (wave * R + r) + col, a.N - 1);
-    wrow[r] = a.qw + (size_t)row[r] * (a.K / 8);
+    wblk[r] = tiled_block(a.qw, n0 + 16 * (wave * R + r), a.N, a.K, lane);
   }
   const int kb0 = q * a.nbs;                 // the plan leaves no split empty
   const int nbl = min(a.nb, kb0 + a.nbs) - kb0;
@@ -221,8 +221,9 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   uint32_t sr[D][R], zr[D][R];
   auto wload = [&](int b, int r, u32x4_t &w, uint32_t &sv, uint32_t &zv) {
     const int kb = kb0 + min(b, nbl - 1);
-    const int off = (kb * 128 + 32 * h < a.K) ? kb * 16 + 4 * h : 0;
-    w = __builtin_nontemporal_load((const u32x4_t *)(wrow[r] + off));
+    // (a piece past K reads the block's first piece instead)
+    const int off = (kb * 128 + 32 * h < a.K) ? kb * 256 : -4 * lane;
+    w = __builtin_nontemporal_load((const u32x4_t *)(wblk[r] + off));
     if constexpr (!PERCH) {
       const int g = (kb * 128) / a.G;
       const size_t e = (size_t)row[r] * a.ngroups + g;

@@ -27,7 +27,7 @@ SPEAR_MAX_DECODE_M = 128
 
 # Every function the header declares, for the export check.
 EXPORTED = (
-    "spear_workspace_bytes", "spear_pack_int4", "spear_linear_decode", "spear_linear_prefill",
+    "spear_workspace_bytes", "spear_pack_int4", "spear_tile_int4", "spear_linear_decode", "spear_linear_prefill",
     "spear_linear", "spear_set_decode_max_m", "spear_get_decode_max_m",
     "spear_set_decode_split_min_m", "spear_get_decode_split_min_m",
     "spear_set_decode_split_min_k", "spear_get_decode_split_min_k", "spear_select_chunk",
@@ -97,6 +97,8 @@ def load_library(path: str = LIB_PATH):
     lib.spear_workspace_bytes.restype = sz
     lib.spear_pack_int4.argtypes = [P, P, i64, i64, P]
     lib.spear_pack_int4.restype = i32
+    lib.spear_tile_int4.argtypes = [P, P, i64, i64, P]
+    lib.spear_tile_int4.restype = i32
     lib.spear_linear_decode.argtypes = [LP, i32, P, P, i32, P, sz, P]
     lib.spear_linear_decode.restype = i32
     lib.spear_linear_decode_noalloc.argtypes = [LP, i32, P, P, i32, P]
@@ -195,7 +197,7 @@ class SpearLayer:
     N: int
     K: int
     group_size: int
-    qweight: object             # int32 [N][K/8]
+    qweight: object             # int32 [qweight_rows(N)][K/8], tiled order
     scales: object              # float16 [N][K/G]
     zeros: object               # float16 [N][K/G]
     rank: int = 0
@@ -236,20 +238,45 @@ def new_workspace(layer: SpearLayer, M: int, device="cuda"):
     return buf[off:off + n]
 
 
+def qweight_rows(N: int) -> int:
+    """Rows of the packed weight tensor: N padded to a multiple of 16 (tiled order)."""
+    return (int(N) + 15) // 16 * 16
+
+
 def spear_pack_int4(q, qweight=None, stream=None):
-    """uint8 codes [N][K] (device) -> int32 packed words [N][K/8] (device)."""
+    """uint8 codes [N][K] (device) -> int32 words [qweight_rows(N)][K/8] in the tiled order."""
     import torch
     _require(q.dim() == 2 and q.dtype == torch.uint8, "q must be a 2-D uint8 tensor [N][K]",
              TypeError)
     _require(q.is_contiguous(), "q must be contiguous")
     N, K = q.shape
-    _require(K % 8 == 0, f"K={K} is not a multiple of 8")
+    _require(K % 32 == 0, f"K={K} is not a multiple of 32")
     if qweight is None:
-        qweight = torch.empty((N, K // 8), dtype=torch.int32, device=q.device)
-    _check_tensor(qweight, "qweight", (N, K // 8), (torch.int32,))
+        qweight = torch.empty((qweight_rows(N), K // 8), dtype=torch.int32, device=q.device)
+    _check_tensor(qweight, "qweight", (qweight_rows(N), K // 8), (torch.int32,))
     _require(q.device.type == "cuda" and qweight.device == q.device,
              f"q and qweight must be on one GPU (got {q.device} and {qweight.device})")
+    _require(qweight.data_ptr() % 16 == 0, "qweight must be 16-byte aligned")
     _check(load_library().spear_pack_int4(_ptr(q), _ptr(qweight), N, K, _stream(stream)))
+    return qweight
+
+
+def spear_tile_int4(words, qweight=None, stream=None):
+    """int32 words packed row after row [N][K/8] (device) -> the tiled order."""
+    import torch
+    _require(words.dim() == 2 and words.dtype == torch.int32,
+             "words must be a 2-D int32 tensor [N][K/8]", TypeError)
+    _require(words.is_contiguous(), "words must be contiguous")
+    N, K = words.shape[0], 8 * words.shape[1]
+    _require(K % 32 == 0, f"K={K} is not a multiple of 32")
+    if qweight is None:
+        qweight = torch.empty((qweight_rows(N), K // 8), dtype=torch.int32, device=words.device)
+    _check_tensor(qweight, "qweight", (qweight_rows(N), K // 8), (torch.int32,))
+    _require(words.device.type == "cuda" and qweight.device == words.device,
+             f"words and qweight must be on one GPU (got {words.device} and {qweight.device})")
+    _require(words.data_ptr() % 16 == 0 and qweight.data_ptr() % 16 == 0,
+             "words and qweight must be 16-byte aligned")
+    _check(load_library().spear_tile_int4(_ptr(words), _ptr(qweight), N, K, _stream(stream)))
     return qweight
 
 
@@ -276,7 +303,7 @@ def _check_layer(layer: "SpearLayer", act) -> None:
     _require(N >= 1 and K >= 1 and G >= 1 and K % G == 0 and K % 8 == 0,
              f"invalid layer geometry N={N} K={K} group_size={G}")
     bits16 = (torch.float16, torch.int16)   # fp16 values or their bit patterns
-    _check_tensor(layer.qweight, "qweight", (N, K // 8), (torch.int32,))
+    _check_tensor(layer.qweight, "qweight", (qweight_rows(N), K // 8), (torch.int32,))
     _check_tensor(layer.scales, "scales", (N, K // G), bits16)
     _check_tensor(layer.zeros, "zeros", (N, K // G), bits16)
     if r > 0:

@@ -133,8 +133,36 @@ def test_pack_rejects_bad_codes(q, exc):
 
 
 def test_pack_rejects_bad_output_and_cpu():
-    q = torch.zeros((4, 16), dtype=torch.uint8)
+    q = torch.zeros((4, 32), dtype=torch.uint8)
     with pytest.raises(ValueError):
-        spear.spear_pack_int4(q, qweight=torch.zeros((4, 3), dtype=torch.int32))
+        spear.spear_pack_int4(q, qweight=torch.zeros((4, 4), dtype=torch.int32))  # unpadded
+    with pytest.raises(ValueError, match="multiple of 32"):
+        spear.spear_pack_int4(torch.zeros((4, 16), dtype=torch.uint8))
     with pytest.raises(ValueError, match="GPU"):
         spear.spear_pack_int4(q)
+
+
+def test_tile_rejects_bad_words():
+    with pytest.raises(TypeError):
+        spear.spear_tile_int4(torch.zeros((4, 4), dtype=torch.int64))
+    with pytest.raises(ValueError, match="multiple of 32"):
+        spear.spear_tile_int4(torch.zeros((4, 2), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        spear.spear_tile_int4(torch.zeros((4, 4), dtype=torch.int32),
+                              qweight=torch.zeros((4, 4), dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        spear.spear_tile_int4(torch.zeros((4, 4), dtype=torch.int32))
+
+
+def test_qweight_rows_padded_to_16():
+    n = 50   # qweight holds qweight_rows(50) = 64 rows in the tiled order
+    assert spear.qweight_rows(n) == 64 and spear.qweight_rows(64) == 64
+    rows = dict(scales=torch.zeros((n, K // G), dtype=torch.float16),
+                zeros=torch.zeros((n, K // G), dtype=torch.float16),
+                B=torch.zeros((n, R), dtype=torch.float16))
+    lay = _layer(N=n, qweight=torch.zeros((64, K // 8), dtype=torch.int32), **rows)
+    with pytest.raises(ValueError, match="GPU"):      # valid shapes: fails only on the device
+        spear.spear_linear_decode(lay, _x())
+    lay = _layer(N=n, qweight=torch.zeros((n, K // 8), dtype=torch.int32), **rows)
+    with pytest.raises(ValueError, match="qweight"):  # unpadded rows
+        spear.spear_linear_decode(lay, _x())

@@ -175,8 +175,15 @@ def test_rejects_bad_io_and_workspace(lib):
     assert pre(ctypes.byref(lay), 0, FAKE * 2, FAKE * 3, 0, FAKE * 4, 1 << 20, None, None) == 0
     assert pre(ctypes.byref(lay), 0, FAKE * 2, FAKE * 3, 2048, FAKE * 4, 64, None, None) == 3
     assert lib.spear_pack_int4(FAKE, FAKE, 4, 12, None) == 1
-    assert lib.spear_pack_int4(None, FAKE, 4, 16, None) == 1
-    assert lib.spear_pack_int4(FAKE, FAKE, 0, 16, None) == 0
+    assert lib.spear_pack_int4(FAKE, FAKE, 4, 16, None) == 1     # K % 32 != 0: no tiled order
+    assert lib.spear_pack_int4(None, FAKE, 4, 32, None) == 1
+    assert lib.spear_pack_int4(FAKE, FAKE + 4, 4, 32, None) == 1  # qweight not 16-byte aligned
+    assert lib.spear_pack_int4(FAKE, FAKE, 0, 32, None) == 0
+    assert lib.spear_tile_int4(FAKE, FAKE * 2, 4, 16, None) == 1
+    assert lib.spear_tile_int4(None, FAKE, 4, 32, None) == 1
+    assert lib.spear_tile_int4(FAKE + 4, FAKE * 2, 4, 32, None) == 1
+    assert lib.spear_tile_int4(FAKE, FAKE + 32, 4, 32, None) == 1  # overlapping buffers
+    assert lib.spear_tile_int4(FAKE, FAKE * 2, 0, 32, None) == 0
 
 
 def test_rank_zero_needs_no_compensator_pointers(lib):

@@ -65,15 +65,37 @@ def decode_split_min_m(m):
 # ---------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("N,K", [(1, 8), (3, 24), (64, 256), (37, 4104), (512, 4096)])
+PACK_SHAPES = [(1, 32), (3, 96), (64, 256), (37, 4128), (512, 4096), (4100, 160)]
+
+
+@pytest.mark.parametrize("N,K", PACK_SHAPES)
 def test_pack_bit_exact(N, K):
     note(f"pack N={N} K={K}")
     rng = np.random.default_rng(N * 7 + K)
     q = rng.integers(0, 256, size=(N, K), dtype=np.uint8)  # high bits must be ignored
     qd = torch.from_numpy(q).to(DEV)
-    words = spear.spear_pack_int4(qd)
+    # every word is written, the zero padding rows included
+    out = torch.full((spear.qweight_rows(N), K // 8), -1, dtype=torch.int32, device=DEV)
+    words = spear.spear_pack_int4(qd, qweight=out)
     torch.cuda.synchronize()
-    assert np.array_equal(words.cpu().numpy(), oracle.pack_int4(q))
+    assert np.array_equal(words.cpu().numpy(), oracle.tile_words(oracle.pack_int4(q)))
+    # unaligned codes take the byte-wise path
+    qu = torch.empty(N * K + 1, dtype=torch.uint8, device=DEV)[1:].view(N, K)
+    qu.copy_(qd)
+    words2 = spear.spear_pack_int4(qu)
+    torch.cuda.synchronize()
+    assert np.array_equal(words2.cpu().numpy(), words.cpu().numpy())
+
+
+@pytest.mark.parametrize("N,K", PACK_SHAPES)
+def test_tile_bit_exact(N, K):
+    note(f"tile N={N} K={K}")
+    rng = np.random.default_rng(N * 11 + K)
+    w = rng.integers(-2**31, 2**31, size=(N, K // 8), dtype=np.int64).astype(np.int32)
+    out = torch.full((spear.qweight_rows(N), K // 8), -1, dtype=torch.int32, device=DEV)
+    t = spear.spear_tile_int4(torch.from_numpy(w).to(DEV), qweight=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(t.cpu().numpy(), oracle.tile_words(w))
 
 
 # ---------------------------------------------------------------------------

@@ -129,6 +129,59 @@ def test_pack_unpack_roundtrip(n, kw, seed):
                 assert u[r, 8 * j + i] == (word >> (4 * i)) & 0xF
 
 
+def _tiled_byte_address(n, k, K):
+    # the tiled order as a wave-load address: 16-row block, 128-code tile of
+    # 1 KB, 16-byte lane piece (quarter h of the tile, row n % 16), word, byte
+    return ((n // 16) * 8 * K + (k // 128) * 1024 + (((k % 128) // 32) * 16 + n % 16) * 16
+            + ((k % 32) // 8) * 4 + (k % 8) // 2)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (16, 128), (37, 160), (50, 416)])
+def test_tile_words_byte_addresses(N, K):
+    rng = np.random.default_rng(N * 1000 + K)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    tiled = oracle.tile_words(oracle.pack_int4(q))
+    n_pad = -(-N // 16) * 16
+    assert tiled.shape == (n_pad, K // 8) and tiled.dtype == np.int32
+    flat = tiled.view(np.uint8).ravel()
+    assert flat.size == (n_pad // 16) * 8 * K
+    seen = np.zeros(flat.size, dtype=bool)
+    for n in range(N):
+        for k in range(K):
+            a = _tiled_byte_address(n, k, K)
+            assert (int(flat[a]) >> (4 * (k % 2))) & 0xF == q[n, k], (n, k)
+            seen[a] = True
+    assert not flat[~seen].any()          # every other byte is row padding, zero
+    assert np.array_equal(oracle.untile_words(tiled, N), oracle.pack_int4(q))
+
+
+def test_tile_words_hand_cases():
+    w = np.arange(1, 1 + 2 * 8, dtype=np.int32).reshape(2, 8)   # N = 2, K = 64: two pieces
+    t = oracle.tile_words(w).ravel()
+    assert t.size == 16 * 8
+    assert t[:8].tolist() == [1, 2, 3, 4, 9, 10, 11, 12]         # piece 0 of rows 0, 1
+    assert not t[8:64].any()                                      # piece 0 of padding rows
+    assert t[64:72].tolist() == [5, 6, 7, 8, 13, 14, 15, 16]     # piece 1 of rows 0, 1
+    assert not t[72:].any()
+    w16 = np.arange(16 * 4, dtype=np.int32).reshape(16, 4)       # K = 32: one piece per row
+    assert np.array_equal(oracle.tile_words(w16), w16)
+
+
+@settings(max_examples=40, deadline=None)
+@given(n=st.integers(1, 40), pieces=st.integers(1, 9), seed=st.integers(0, 2**31 - 1))
+def test_tile_untile_roundtrip(n, pieces, seed):
+    rng = np.random.default_rng(seed)
+    w = rng.integers(-2**31, 2**31, size=(n, 4 * pieces), dtype=np.int64).astype(np.int32)
+    t = oracle.tile_words(w)
+    assert np.array_equal(oracle.untile_words(t, n), w)
+    assert sorted(t.ravel().tolist()) == sorted(w.ravel().tolist() + [0] * (t.size - w.size))
+
+
+def test_tile_words_rejects_partial_piece():
+    with pytest.raises(ValueError):
+        oracle.tile_words(np.zeros((2, 6), dtype=np.int32))
+
+
 def test_pack_rejects_ragged_k():
     with pytest.raises(ValueError):
         oracle.pack_int4(np.zeros((2, 12), dtype=np.uint8))
