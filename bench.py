@@ -450,6 +450,81 @@ def rank_gate_context(torch, device):
 
 
 PROMPT = 8192  # prompt length for the serving leg's time-to-first-token figures
+STREAM_REQUESTS = 12          # request stream: prompts 512..4096 tokens (multiples of 256),
+STREAM_GAP_MS = 20.0          # 16..48 output tokens, exponential gaps between arrivals
+STREAM_DENSITIES = (0, 4, 16, 32)
+STREAM_STATIC = (512, 1024, 2048)
+# inter-token targets: the pages quote 16 and 22 ms for whole models on their hardware; on
+# this 96-linear stack the predicted steps cross 12 ms (1024-token chunks) and 20 ms (2048)
+# between compensator densities 0 and 32, so those targets show the selector adapting
+STREAM_SLOS_MS = (12.0, 16.0, 20.0)
+
+
+def simulate_stream(requests, choose_chunk, run_step, max_batch=32):
+    """Continuous batching over a request stream, on a virtual clock driven by measured steps.
+
+    requests: (arrival_ms, prompt_tokens, output_tokens) per request, in arrival order.
+    Requests are prefilled one at a time, first come first served, a chunk per step;
+    every request past its prefill decodes one token per step, at most max_batch of them
+    (a request starts its prefill only while fewer than max_batch are past it).
+    choose_chunk(n_decoding) gives the step's chunk size; run_step(chunk_tokens,
+    n_decoding) runs the step and returns its time in ms, which advances the clock.  A
+    request's first token comes at the end of the step that holds its last prompt chunk
+    (time to first token = that time minus its arrival); each later token comes one step
+    after the previous one (inter-token latency = that step's time)."""
+    pending = sorted(range(len(requests)), key=lambda i: requests[i][0])
+    t, nxt = 0.0, 0
+    fifo, running, last, left = [], [], {}, {}
+    cur, cur_left = None, 0
+    ttft, itl, steps, chunks_used = [], [], 0, {}
+    done = 0
+    while done < len(requests):
+        while nxt < len(pending) and requests[pending[nxt]][0] <= t:
+            fifo.append(pending[nxt])
+            nxt += 1
+        if cur is None and fifo and len(running) < max_batch:
+            cur = fifo.pop(0)
+            cur_left = requests[cur][1]
+        n = len(running)
+        c = min(choose_chunk(n), cur_left) if cur is not None else 0
+        if c == 0 and n == 0:
+            t = max(t, requests[pending[nxt]][0])   # idle until the next arrival
+            continue
+        t += run_step(c, n)
+        steps += 1
+        if c:
+            chunks_used[c] = chunks_used.get(c, 0) + 1
+        for r in list(running):
+            itl.append(t - last[r])
+            last[r] = t
+            left[r] -= 1
+            if left[r] == 0:
+                running.remove(r)
+                done += 1
+        if cur is not None:
+            cur_left -= c
+            if cur_left == 0:
+                ttft.append(t - requests[cur][0])
+                if requests[cur][2] > 1:
+                    running.append(cur)
+                    last[cur], left[cur] = t, requests[cur][2] - 1
+                else:
+                    done += 1
+                cur = None
+    return {"ttft": ttft, "itl": itl, "steps": steps, "makespan_ms": t, "chunks": chunks_used}
+
+
+def stream_summary(res, slos, requests):
+    ttft, itl = np.asarray(res["ttft"]), np.asarray(res["itl"])
+    out = {"ttft_ms_mean": round(float(ttft.mean()), 2), "ttft_ms_p90": round(float(np.percentile(ttft, 90)), 2),
+           "itl_ms_p50": round(float(np.percentile(itl, 50)), 3), "itl_ms_p99": round(float(np.percentile(itl, 99)), 3),
+           "itl_ms_max": round(float(itl.max()), 3),
+           "steps": res["steps"], "makespan_ms": round(res["makespan_ms"], 1),
+           "tokens_per_s": round(1e3 * sum(p + o for _, p, o in requests) / res["makespan_ms"], 1),
+           "chunk_steps": {str(k): v for k, v in sorted(res["chunks"].items())}}
+    for slo in slos:
+        out[f"itl_over_{slo:g}ms_pct"] = round(100.0 * float((itl > slo).mean()), 2)
+    return out
 
 
 def serving_context(torch, device):
@@ -459,7 +534,10 @@ def serving_context(torch, device):
     every linear.  A latency table measured per (shape, compensated or not, C or decode)
     predicts the step time at every density; the chunk selector picks C for each budget.  At
     the configured density (4 blocks) every budget's chosen step is run and timed; at the
-    other densities (0, 8, 16, 32) the step chosen for a 16 ms budget is."""
+    other densities (0, 8, 16, 32) the step chosen for a 16 ms budget is.  Last, a seeded
+    request stream runs under continuous batching with static chunk sizes and with the
+    SLO-aware selector, and its measured time to first token and inter-token latency are
+    reported per density (simulate_stream)."""
     from quantized_gemm_error_amd import spear, synth
     w = synth.WORKLOADS["llama7b-stack-serving"]
     gen = torch.Generator(device=device)
@@ -539,6 +617,67 @@ def serving_context(torch, device):
                                                      "merged": round(measured(C, ecs, merged=True), 3)}
                                             for C in chunks}
         out["densities"][str(d)] = rec
+
+    # A seeded request stream under continuous batching: each step one prefill chunk and
+    # one decode token per running request, every step run from captured graphs and
+    # timed.  Static chunk sizes against the SLO-aware selector (the largest chunk whose
+    # predicted step time, from the table above, meets the inter-token target; the
+    # largest chunk when nothing is decoding), at several compensator densities.
+    rng = np.random.default_rng(w["seed"] + 1)
+    n_req = STREAM_REQUESTS
+    requests = [(float(a), int(p) * 256, int(o)) for a, p, o in
+                zip(np.cumsum(rng.exponential(STREAM_GAP_MS, n_req)), rng.integers(2, 17, n_req),
+                    rng.integers(16, 49, n_req))]
+    sizes = sorted({256 * k for k in range(1, max(chunks) // 256 + 1)})
+    stream = torch.cuda.Stream()
+    stream_out = {"requests": n_req, "mean_gap_ms": STREAM_GAP_MS,
+                  "prompt_tokens": [p for _, p, _ in requests], "output_tokens": [o for _, _, o in requests],
+                  "slo_ms": list(STREAM_SLOS_MS), "densities": {}}
+    for d in STREAM_DENSITIES:
+        ecs = ec_sets[d] if d in ec_sets else {int(b) for b in synth.ec_block_indices(nb, d, w["seed"])}
+        gp, gd = {}, {}
+        for c in sizes:
+            gp[c] = capture_graphs(torch, lambda _p: [call(b, si, c, stream, b in ecs) for b in range(nb)
+                                                       for si in range(len(shapes))], 1, stream)[0]
+        for n in range(1, n_dec + 1):
+            gd[n] = capture_graphs(torch, lambda _p: [call(b, si, n, stream, b in ecs) for b in range(nb)
+                                                       for si in range(len(shapes))], 1, stream)[0]
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def run_step(c, n):
+            with torch.cuda.stream(stream):
+                ev0.record(stream)
+                if c:
+                    gp[c].replay()
+                if n:
+                    gd[n].replay()
+                ev1.record(stream)
+            ev1.synchronize()
+            return ev0.elapsed_time(ev1)
+
+        for _ in range(3):                          # settle the clocks
+            run_step(max(chunks), n_dec)
+        pred_pre = {C: sum(lut[(si, b in ecs, C)] for b in range(nb) for si in range(len(shapes)))
+                    for C in chunks}
+        pred_dec = sum(lut[(si, b in ecs, n_dec)] for b in range(nb) for si in range(len(shapes)))
+        rec = {"predicted_step_ms": {str(C): round(pred_pre[C] + pred_dec, 3) for C in chunks}}
+        policies = {f"static_{C}": (lambda C: lambda n: C)(C) for C in STREAM_STATIC}
+
+        def slo_policy(slo):
+            def choose(n):
+                if n == 0:
+                    return max(chunks)
+                C, _violated = spear.spear_select_chunk(chunks, [pred_pre[C] + pred_dec for C in chunks], slo)
+                return C
+            return choose
+        for slo in STREAM_SLOS_MS:
+            policies[f"slo_{slo:g}ms"] = slo_policy(slo)
+        for name, choose in policies.items():
+            rec[name] = stream_summary(simulate_stream(requests, choose, run_step, max_batch=n_dec),
+                                       STREAM_SLOS_MS, requests)
+        stream_out["densities"][str(d)] = rec
+        del gp, gd
+    out["request_stream"] = stream_out
     record_flags("serving", [ws])
     del stack, plain, xs, ys, ws, wbuf
     torch.cuda.empty_cache()
@@ -926,6 +1065,9 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the Llama-7B prefill calls (M = 2048, bf16) and print them: "
                          "the command that the prefill kernel profiles are taken with")
+    ap.add_argument("--serving-only", action="store_true",
+                    help="run only the serving-stack leg (latency table, chunk selector, request "
+                         "stream) and print it")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, out_dir=os.path.join(ROOT, "profiles"))
@@ -947,6 +1089,9 @@ def main():
 
     if args.prefill_only:
         print(json.dumps({"prefill_llama7b_bf16_M2048": prefill_context(torch, dev)}), flush=True)
+        return
+    if args.serving_only:
+        print(json.dumps({"serving_stack_7b": serving_context(torch, dev)}), flush=True)
         return
 
     log("building decode workload")
