@@ -59,6 +59,18 @@ __device__ __forceinline__ const uint32_t *tiled_block(const uint32_t *qw, int n
   return qw + (size_t)rb * 2 * K + 4 * lane;
 }
 
+// Workgroup barrier for LDS only: this wave's LDS operations complete
+// (lgkmcnt(0)), then s_barrier.  __syncthreads() also carries a release fence
+// that waits for every outstanding global load (vmcnt(0)), which would drain
+// the weight and activation prefetches at every staged chunk.  The signal
+// fences keep the compiler from moving memory operations across.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Per-row zero-point constant for dequant_word.
 //   fp16: packed pair of -(1024 + z) (exact: 1024 + z is an integer < 2048).
 //   bf16: 2^23 + z as an fp32 bit pattern.

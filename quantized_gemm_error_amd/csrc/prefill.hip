@@ -109,6 +109,159 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t &hi, uint16_t &lo) 
   lo = bitcast<uint16_t>((__bf16)(v - (float)h));
 }
 
+
+constexpr int kEpiRc = 32;           // ranks per epilogue chunk: the K of one 16x16x32 MFMA
+// LDS row stride of a chunk's bf16 operands (halves): 24 dwords, so a
+// fragment read's 16 rows x 2 column groups fall on distinct banks
+constexpr int kEpiStr = kEpiRc + 16;
+static_assert(2 * BM * kEpiStr <= BM * LSTR, "epilogue U hi/lo fit the activation tile");
+static_assert(2 * BN * kEpiStr <= BN * WSTR, "epilogue B hi/lo fit the weight tile");
+
+// ---------------------------------------------------------------------------
+// Compensator sums: Tp[ksi][m][j] = sum over split ksi's K range of
+// [A; w_g][j][k] x[m][k], j = 0..rank.
+//
+// Workgroup (blk, ksi) takes kEcTok = 32 tokens (two MFMA row blocks) and K
+// split ksi of ks; its eight waves take interleaved 32-wide K steps.  Up to
+// kEcRb 16-row blocks of [A; w_g] are accumulated together, so each weight
+// piece feeds both token blocks and each activation piece feeds kEcRb MFMAs;
+// each wave keeps kEcU steps of loads in flight before it multiplies.
+// ---------------------------------------------------------------------------
+struct EcArgs {
+  const uint16_t *x, *A, *wg;
+  int K, M, rank, rows, rp1, ks;  // rows of [A; w_g]: rank + 1, or rank (per-rank gate)
+  float *Tp;  // [ks][M][rp1]
+  // ks == 1 with the scalar gate: U = diag(g) (X A^T) written here directly
+  // (zeros in columns rank .. rp1-1), and no partials
+  float *U;
+  float b_gate;
+};
+
+constexpr int kEcWaves = 8, kEcRb = 3, kEcU = 4, kEcTok = 32, kEcMb = kEcTok / 16;
+// rows of [A; w_g] round up to 16: up to 16 * ceil((SPEAR_MAX_RANK + 1) / 16) = 144
+constexpr int kTzStride = 145;
+static_assert(kTzStride > 16 * ((SPEAR_MAX_RANK + 1 + 15) / 16), "tz stride");
+
+// One compensator block: tokens blk * kEcTok .. + kEcTok, K split ksi of a.ks,
+// by WAVES waves (the stand-alone kernel's eight, or the four of a producer
+// workgroup in the GEMM launch, whose sums other workgroups of that launch
+// read: AGENT stores them with agent-scope stores).  red and tz are LDS.
+template <int DT, int WAVES, bool AGENT>
+__device__ void ec_block(const EcArgs &a, int blk, int ksi, f32x4_t (*red)[kEcRb][kEcMb][64],
+                         float (*tz)[kTzStride], int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, h = lane >> 4;
+  const int m0 = blk * kEcTok;
+  // A-operand rows of this lane: tokens m0 + col + 16 mb; rows past M repeat
+  // M - 1 (MFMA output rows depend only on their own A rows, and those are
+  // never stored)
+  const uint16_t *xrow[kEcMb];
+#pragma unroll
+  for (int mb = 0; mb < kEcMb; ++mb) xrow[mb] = a.x + (size_t)min(m0 + col + 16 * mb, a.M - 1) * a.K;
+  const int rb_a = (a.rows + 15) / 16;
+  const int nsteps = a.K / 32;
+  const int per = (nsteps + a.ks - 1) / a.ks;
+  const int s_lo = ksi * per, s_hi = min(nsteps, s_lo + per);
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+  for (int rb0 = 0; rb0 < rb_a; rb0 += kEcRb) {
+    const uint16_t *arow[kEcRb];
+    bool jin[kEcRb];
+#pragma unroll
+    for (int r = 0; r < kEcRb; ++r) {
+      const int j = (rb0 + r) * 16 + col;
+      jin[r] = rb0 + r < rb_a && j < a.rows;
+      // j >= rank: w_g, or (per-rank gate, no w_g) any valid row; masked past the rows
+      arow[r] = (j < a.rank) ? a.A + (size_t)j * a.K : (a.wg ? a.wg : a.A);
+    }
+    f32x4_t acc[kEcRb][kEcMb];
+#pragma unroll
+    for (int r = 0; r < kEcRb; ++r)
+#pragma unroll
+      for (int mb = 0; mb < kEcMb; ++mb) acc[r][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int s0 = s_lo + wave; s0 < s_hi; s0 += WAVES * kEcU) {
+      u32x4_t xo[kEcU][kEcMb], ao[kEcU][kEcRb];
+#pragma unroll
+      for (int u = 0; u < kEcU; ++u) {
+        const int k = min(s0 + WAVES * u, s_hi - 1) * 32 + 8 * h;
+#pragma unroll
+        for (int mb = 0; mb < kEcMb; ++mb) xo[u][mb] = *(const u32x4_t *)(xrow[mb] + k);
+#pragma unroll
+        for (int r = 0; r < kEcRb; ++r) ao[u][r] = *(const u32x4_t *)(arow[r] + k);
+      }
+#pragma unroll
+      for (int u = 0; u < kEcU; ++u) {
+        if (s0 + WAVES * u < s_hi) {
+#pragma unroll
+          for (int r = 0; r < kEcRb; ++r) {
+            const u32x4_t b = jin[r] ? ao[u][r] : zero;
+#pragma unroll
+            for (int mb = 0; mb < kEcMb; ++mb) acc[r][mb] = mfma_16x16x32<DT>(xo[u][mb], b, acc[r][mb]);
+          }
+        }
+      }
+    }
+    // fixed-order sum over the waves: wave 0's own, then 1..7
+    if (wave > 0) {
+#pragma unroll
+      for (int r = 0; r < kEcRb; ++r)
+#pragma unroll
+        for (int mb = 0; mb < kEcMb; ++mb) red[wave][r][mb][lane] = acc[r][mb];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int r = 0; r < kEcRb; ++r) {
+        if (rb0 + r < rb_a) {
+#pragma unroll
+          for (int mb = 0; mb < kEcMb; ++mb) {
+            f32x4_t v = acc[r][mb];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) v = v + red[w][r][mb][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tz[16 * mb + 4 * h + e][(rb0 + r) * 16 + col] = v[e];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+
+  if (a.U) {
+    // the whole of K in this workgroup: U = g t for its tokens, g from row rank
+    const int nval = kEcTok * a.rp1;
+    for (int i = tid; i < nval; i += 64 * WAVES) {
+      const int mm = i / a.rp1, j = i - mm * a.rp1;
+      if (m0 + mm < a.M)
+        a.U[(size_t)(m0 + mm) * a.rp1 + j] =
+            j < a.rank ? gate_sigmoid(tz[mm][a.rank] + a.b_gate) * tz[mm][j] : 0.f;
+    }
+    return;
+  }
+  // this split's sums, rows 0..rows-1 of its tokens
+  const int nval = kEcTok * a.rows;
+  float *tp = a.Tp + ((size_t)ksi * a.M + m0) * a.rp1;
+  for (int i = tid; i < nval; i += 64 * WAVES) {
+    const int mm = i / a.rows, j = i - mm * a.rows;
+    if (m0 + mm < a.M) {
+      if constexpr (AGENT)  // read by other workgroups of the same launch
+        __hip_atomic_store((uint32_t *)&tp[(size_t)mm * a.rp1 + j], bitcast<uint32_t>(tz[mm][j]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        tp[(size_t)mm * a.rp1 + j] = tz[mm][j];
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(64 * kEcWaves) void prefill_ec_kernel(EcArgs a) {
+  __shared__ f32x4_t red[kEcWaves][kEcRb][kEcMb][64];
+  __shared__ float tz[kEcTok][kTzStride];
+  ec_block<DT, kEcWaves, false>(a, blockIdx.x / a.ks, blockIdx.x % a.ks, red, tz, threadIdx.x);
+}
+
 struct GemmArgs {
   const uint32_t *qw;
   const uint16_t *scales, *zeros;
@@ -119,14 +272,16 @@ struct GemmArgs {
   const uint16_t *B;  // EPI: [N][rank]
   int ks;             // SPLIT: K splits (blockIdx.z), each a contiguous range of k-blocks
   float *part;        // SPLIT: [ks][M][N] fp32 partial outputs
+  // PROD (the concurrent schedule): the first nprod workgroups of a 1-D grid
+  // (nprod a multiple of 8; those past nprod_real only count themselves in)
+  // compute the compensator's K-split sums ec.Tp, and the ntn x ntm GEMM tiles
+  // after them read those sums in their epilogue once every producer is in
+  int nprod, nprod_real, ntn, ntm;
+  EcArgs ec;
+  WsHeader *hdr;
+  uint32_t spin_limit;  // polls of the producers' count before a tile computes the sums itself
+  float *Tfb;           // [M][rp1]: the sums of a tile whose wait expired
 };
-
-constexpr int kEpiRc = 32;           // ranks per epilogue chunk: the K of one 16x16x32 MFMA
-// LDS row stride of a chunk's bf16 operands (halves): 24 dwords, so a
-// fragment read's 16 rows x 2 column groups fall on distinct banks
-constexpr int kEpiStr = kEpiRc + 16;
-static_assert(2 * BM * kEpiStr <= BM * LSTR, "epilogue U hi/lo fit the activation tile");
-static_assert(2 * BN * kEpiStr <= BN * WSTR, "epilogue B hi/lo fit the weight tile");
 
 // Output tile of this workgroup.  Workgroups go to the eight XCDs in turn
 // (linear id mod 8) and each XCD has its own L2, so the tiles are renumbered:
@@ -135,10 +290,8 @@ static_assert(2 * BN * kEpiStr <= BN * WSTR, "epilogue B hi/lo fit the weight ti
 // workgroups that one XCD holds at a time then cover a compact block of the
 // output and share its activation rows and weight columns in that L2.
 constexpr int kGroupM = 8;
-__device__ __forceinline__ void gemm_tile(int &tm, int &tn) {
-  const int ntn = gridDim.x, ntm = gridDim.y;
+__device__ __forceinline__ void gemm_tile(int L, int ntn, int ntm, int &tm, int &tn) {
   const int T = ntn * ntm;
-  const int L = blockIdx.y * ntn + blockIdx.x;
   const int c = L & 7;
   int p = L >> 3;  // after the tiles of XCDs 0 .. c-1; XCD c' holds ceil((T - c') / 8)
   for (int cc = 0; cc < c; ++cc) p += (T - cc + 7) >> 3;
@@ -157,18 +310,67 @@ __device__ __forceinline__ void gemm_tile(int &tm, int &tn) {
 __device__ __forceinline__ int wpiece_row(int p) { return 16 * (p >> 6) + (p & 15); }
 __device__ __forceinline__ int wpiece_quarter(int p) { return (p & 63) >> 4; }
 
-template <int DT, bool PERCH, bool EPI, bool SPLIT>
+// Count this workgroup out of a PROD launch; the last one resets the
+// producers' count and these counters.  Workgroup b counts into slot b % 8;
+// the one that completes a slot counts the slot into the top counter, and
+// the one that completes the top counter is last overall.
+__device__ void prod_finish(WsHeader *hdr) {
+  const uint32_t g = gridDim.x, b = blockIdx.x, slot = b % 8;
+  const uint32_t in_slot = (g - 1 - slot) / 8 + 1;
+  const uint32_t old = __hip_atomic_fetch_add(&hdr->done[slot].v, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  if (old + 1 != in_slot) return;
+  const uint32_t slots = g < 8 ? g : 8;
+  const uint32_t top = __hip_atomic_fetch_add(&hdr->done_top.v, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  if (top + 1 != slots) return;
+  __hip_atomic_store(&hdr->arrive.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&hdr->done_top.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < 8; ++i)
+    __hip_atomic_store(&hdr->done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Completion of this wave's agent-scope stores (s_waitcnt vmcnt(0); expcnt
+// and lgkmcnt left at their maxima), fenced against compiler motion.
+__device__ __forceinline__ void stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int DT, bool PERCH, bool EPI, bool SPLIT, bool PROD = false>
 __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
   static_assert(!(EPI && SPLIT), "split tiles are finished by prefill_finish_kernel");
+  static_assert(!PROD || (EPI && !SPLIT), "producers serve the epilogue of unsplit tiles");
   __shared__ __align__(16) uint16_t xs[BM * LSTR];
   __shared__ __align__(16) uint16_t wsm[BN * WSTR];
   __shared__ float ss[BN];
+  __shared__ int vote;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, h = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
-  gemm_tile(tm, tn);
+  if constexpr (PROD) {
+    if ((int)blockIdx.x < a.nprod) {
+      // a compensator producer: one (32-token block, K split) of the sums
+      static_assert(sizeof(f32x4_t) * 4 * kEcRb * kEcMb * 64 <= sizeof(xs), "producer red in xs");
+      static_assert(sizeof(float) * kEcTok * kTzStride <= sizeof(wsm), "producer tz in wsm");
+      if ((int)blockIdx.x < a.nprod_real)
+        ec_block<DT, 4, true>(a.ec, blockIdx.x / a.ec.ks, blockIdx.x % a.ec.ks,
+                              (f32x4_t(*)[kEcRb][kEcMb][64])xs, (float(*)[kTzStride])wsm, tid);
+      stores_done();
+      __syncthreads();
+      if (tid == 0) {
+        __hip_atomic_fetch_add(&a.hdr->arrive.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prod_finish(a.hdr);
+      }
+      return;
+    }
+    gemm_tile(blockIdx.x - a.nprod, a.ntn, a.ntm, tm, tn);
+  } else {
+    gemm_tile(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, tm, tn);
+  }
   const int n0 = tn * BN, m0 = tm * BM;
   const int nkb = (a.K + BK - 1) / BK;
   const int kw = a.K / 8;
@@ -324,13 +526,56 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
   f32x4_t u_pre[4];
   u16x8_t b_pre[2];
   const bool bvec = (a.u.rank % 8) == 0 && ((uintptr_t)a.B % 16) == 0;
+  // PROD: U is formed here from the producers' K-split sums (or, when the
+  // wait for them expired, from this tile's own full sums in Tfb), exactly as
+  // prefill_u_kernel forms it: each sum in split order, g = sigmoid(z + b_g)
+  // from the gate row, u = g t.  The sums are read with the sc1 policy, which
+  // reads across the XCDs' L2 caches.
+  bool expired = false;
+  float gv[4] = {0.f, 0.f, 0.f, 0.f};
   auto epi_load = [&](int j0) {
     const UView &u = a.u;
+    if constexpr (PROD) {
+      const float *T = expired ? a.Tfb : a.ec.Tp;
+      const int ks = expired ? 1 : a.ec.ks;
+      const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)T, (short)0, ks * a.M * u.rp1 * 4, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = tid + 256 * i;  // BM rows x 8 pieces
-      const int r = p >> 3, j = j0 + 4 * (p & 7);
-      u_pre[i] = *(const f32x4_t *)(u.U + (size_t)min(m0 + r, a.M - 1) * u.rp1 + min(j, u.rp1 - 4));
+      for (int i = 0; i < 4; ++i) {
+        const int p = tid + 256 * i;  // BM rows x 8 pieces
+        const int r = p >> 3, j = min(j0 + 4 * (p & 7), u.rp1 - 4);
+        const int m = min(m0 + r, a.M - 1);
+        f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+        float z = 0.f;
+        for (int q0 = 0; q0 < ks; q0 += 4) {  // four splits' loads in flight at a time
+          f32x4_t tv[4];
+          float zv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = (min(q0 + q, ks - 1) * a.M + m) * u.rp1;
+            tv[q] = bitcast<f32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(tr, (row + j) * 4, 0, 16));
+            zv[q] = j0 == 0 ? bitcast<float>(__builtin_amdgcn_raw_buffer_load_b32(
+                                  tr, (row + u.rank) * 4, 0, 16))
+                            : 0.f;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q0 + q < ks) {
+              t += tv[q];
+              z += zv[q];
+            }
+        }
+        if (j0 == 0) gv[i] = gate_sigmoid(z + a.ec.b_gate);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) u_pre[i][c] = (j + c < u.rank) ? gv[i] * t[c] : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = tid + 256 * i;  // BM rows x 8 pieces
+        const int r = p >> 3, j = j0 + 4 * (p & 7);
+        u_pre[i] = *(const f32x4_t *)(u.U + (size_t)min(m0 + r, a.M - 1) * u.rp1 + min(j, u.rp1 - 4));
+      }
     }
     if (bvec) {
 #pragma unroll
@@ -351,15 +596,79 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
     kb_lo = min(nkb, (int)blockIdx.z * per);
     kb_hi = min(nkb, kb_lo + per);
   }
+  // PROD: wave 0 reads the producers' count two blocks before the last one,
+  // so that the value is in by the last block
+  uint32_t arrived = 0;
   if (kb_lo < kb_hi) gload(kb_lo);
   for (int kb = kb_lo; kb + 1 < kb_hi; ++kb) {
+    if constexpr (PROD) {
+      if (wave == 0 && kb == max(kb_lo, kb_hi - 3))
+        arrived = __hip_atomic_load(&a.hdr->arrive.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     lstore();
     __syncthreads();
     gload(kb + 1);
     compute();
   }
-  if (kb_lo < kb_hi) {
+  if constexpr (PROD) {
+    // If every producer was in when wave 0 read the count (a single block:
+    // read now), the epilogue's sums are loaded before the last block's MFMAs,
+    // behind which they stay in flight.  Otherwise the count is polled after
+    // them: a bounded wait (spin_limit polls), and on expiry this tile
+    // computes the sums of its tokens itself.
+    if (wave == 0 && kb_hi - kb_lo < 2)
+      arrived = __hip_atomic_load(&a.hdr->arrive.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool early = false;
+    if (kb_lo < kb_hi) {
+      __syncthreads();
+      lstore();
+      if (tid == 0) vote = (a.spin_limit > 0 && arrived >= (uint32_t)a.nprod) ? 2 : 0;
+      __syncthreads();
+      early = vote == 2;
+      if (early && a.u.rank > 0) epi_load(0);
+      compute();
+    }
+    if (!early && tid == 0) {
+      // (a limit of 0 polls: no wait at all, every tile computes its own sums)
+      int ex = a.spin_limit == 0 ? 1 : 0;
+      for (uint32_t it = 0; !ex && arrived < (uint32_t)a.nprod; ++it) {
+        if (it >= a.spin_limit) {
+          ex = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        arrived = __hip_atomic_load(&a.hdr->arrive.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (ex)
+        __hip_atomic_fetch_or(&a.hdr->flags.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      vote = ex;
+    }
+    __syncthreads();
+    expired = !early && vote == 1;
+    if (expired) {
+      // [A; w_g] x over all of K for this tile's tokens, into Tfb (tiles of
+      // one token band write the same values there, computed the same way)
+      const EcArgs &e = a.ec;
+      const int nval = min(BM, a.M - m0) * e.rows;
+      for (int i = tid; i < nval; i += 256) {
+        const int mm = i / e.rows, j = i - mm * e.rows;
+        const uint16_t *arow = j < e.rank ? e.A + (size_t)j * a.K : e.wg;
+        const uint16_t *xrow = a.x + (size_t)(m0 + mm) * a.K;
+        float t = 0.f;
+        for (int k = 0; k < a.K; k += 8) {
+          const u16x8_t av = *(const u16x8_t *)(arow + k);
+          const u16x8_t xv = *(const u16x8_t *)(xrow + k);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) t += to_f32<DT>(av[c]) * to_f32<DT>(xv[c]);
+        }
+        a.Tfb[(size_t)(m0 + mm) * e.rp1 + j] = t;
+      }
+      stores_done();
+      __syncthreads();
+    }
+    if (!early && a.u.rank > 0) epi_load(0);
+  } else if (kb_lo < kb_hi) {
     __syncthreads();
     lstore();
     __syncthreads();
@@ -484,137 +793,11 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(GemmArgs a) {
       }
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Compensator sums: Tp[ksi][m][j] = sum over split ksi's K range of
-// [A; w_g][j][k] x[m][k], j = 0..rank.
-//
-// Workgroup (blk, ksi) takes kEcTok = 32 tokens (two MFMA row blocks) and K
-// split ksi of ks; its eight waves take interleaved 32-wide K steps.  Up to
-// kEcRb 16-row blocks of [A; w_g] are accumulated together, so each weight
-// piece feeds both token blocks and each activation piece feeds kEcRb MFMAs;
-// each wave keeps kEcU steps of loads in flight before it multiplies.
-// ---------------------------------------------------------------------------
-struct EcArgs {
-  const uint16_t *x, *A, *wg;
-  int K, M, rank, rows, rp1, ks;  // rows of [A; w_g]: rank + 1, or rank (per-rank gate)
-  float *Tp;  // [ks][M][rp1]
-  // ks == 1 with the scalar gate: U = diag(g) (X A^T) written here directly
-  // (zeros in columns rank .. rp1-1), and no partials
-  float *U;
-  float b_gate;
-};
-
-constexpr int kEcWaves = 8, kEcRb = 3, kEcU = 4, kEcTok = 32, kEcMb = kEcTok / 16;
-// rows of [A; w_g] round up to 16: up to 16 * ceil((SPEAR_MAX_RANK + 1) / 16) = 144
-constexpr int kTzStride = 145;
-static_assert(kTzStride > 16 * ((SPEAR_MAX_RANK + 1 + 15) / 16), "tz stride");
-
-template <int DT>
-__global__ __launch_bounds__(64 * kEcWaves) void prefill_ec_kernel(EcArgs a) {
-  __shared__ f32x4_t red[kEcWaves][kEcRb][kEcMb][64];
-  __shared__ float tz[kEcTok][kTzStride];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 15, h = lane >> 4;
-  const int blk = blockIdx.x / a.ks, ksi = blockIdx.x % a.ks;
-  const int m0 = blk * kEcTok;
-  // A-operand rows of this lane: tokens m0 + col + 16 mb; rows past M repeat
-  // M - 1 (MFMA output rows depend only on their own A rows, and those are
-  // never stored)
-  const uint16_t *xrow[kEcMb];
-#pragma unroll
-  for (int mb = 0; mb < kEcMb; ++mb) xrow[mb] = a.x + (size_t)min(m0 + col + 16 * mb, a.M - 1) * a.K;
-  const int rb_a = (a.rows + 15) / 16;
-  const int nsteps = a.K / 32;
-  const int per = (nsteps + a.ks - 1) / a.ks;
-  const int s_lo = ksi * per, s_hi = min(nsteps, s_lo + per);
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-  for (int rb0 = 0; rb0 < rb_a; rb0 += kEcRb) {
-    const uint16_t *arow[kEcRb];
-    bool jin[kEcRb];
-#pragma unroll
-    for (int r = 0; r < kEcRb; ++r) {
-      const int j = (rb0 + r) * 16 + col;
-      jin[r] = rb0 + r < rb_a && j < a.rows;
-      // j >= rank: w_g, or (per-rank gate, no w_g) any valid row; masked past the rows
-      arow[r] = (j < a.rank) ? a.A + (size_t)j * a.K : (a.wg ? a.wg : a.A);
-    }
-    f32x4_t acc[kEcRb][kEcMb];
-#pragma unroll
-    for (int r = 0; r < kEcRb; ++r)
-#pragma unroll
-      for (int mb = 0; mb < kEcMb; ++mb) acc[r][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int s0 = s_lo + wave; s0 < s_hi; s0 += kEcWaves * kEcU) {
-      u32x4_t xo[kEcU][kEcMb], ao[kEcU][kEcRb];
-#pragma unroll
-      for (int u = 0; u < kEcU; ++u) {
-        const int k = min(s0 + kEcWaves * u, s_hi - 1) * 32 + 8 * h;
-#pragma unroll
-        for (int mb = 0; mb < kEcMb; ++mb) xo[u][mb] = *(const u32x4_t *)(xrow[mb] + k);
-#pragma unroll
-        for (int r = 0; r < kEcRb; ++r) ao[u][r] = *(const u32x4_t *)(arow[r] + k);
-      }
-#pragma unroll
-      for (int u = 0; u < kEcU; ++u) {
-        if (s0 + kEcWaves * u < s_hi) {
-#pragma unroll
-          for (int r = 0; r < kEcRb; ++r) {
-            const u32x4_t b = jin[r] ? ao[u][r] : zero;
-#pragma unroll
-            for (int mb = 0; mb < kEcMb; ++mb) acc[r][mb] = mfma_16x16x32<DT>(xo[u][mb], b, acc[r][mb]);
-          }
-        }
-      }
-    }
-    // fixed-order sum over the waves: wave 0's own, then 1..7
-    if (wave > 0) {
-#pragma unroll
-      for (int r = 0; r < kEcRb; ++r)
-#pragma unroll
-        for (int mb = 0; mb < kEcMb; ++mb) red[wave][r][mb][lane] = acc[r][mb];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int r = 0; r < kEcRb; ++r) {
-        if (rb0 + r < rb_a) {
-#pragma unroll
-          for (int mb = 0; mb < kEcMb; ++mb) {
-            f32x4_t v = acc[r][mb];
-#pragma unroll
-            for (int w = 1; w < kEcWaves; ++w) v = v + red[w][r][mb][lane];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tz[16 * mb + 4 * h + e][(rb0 + r) * 16 + col] = v[e];
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-
-  if (a.U) {
-    // the whole of K in this workgroup: U = g t for its tokens, g from row rank
-    const int nval = kEcTok * a.rp1;
-    for (int i = tid; i < nval; i += 64 * kEcWaves) {
-      const int mm = i / a.rp1, j = i - mm * a.rp1;
-      if (m0 + mm < a.M)
-        a.U[(size_t)(m0 + mm) * a.rp1 + j] =
-            j < a.rank ? gate_sigmoid(tz[mm][a.rank] + a.b_gate) * tz[mm][j] : 0.f;
-    }
-    return;
-  }
-  // this split's sums, rows 0..rows-1 of its tokens
-  const int nval = kEcTok * a.rows;
-  float *tp = a.Tp + ((size_t)ksi * a.M + m0) * a.rp1;
-  for (int i = tid; i < nval; i += 64 * kEcWaves) {
-    const int mm = i / a.rows, j = i - mm * a.rows;
-    if (m0 + mm < a.M) tp[(size_t)mm * a.rp1 + j] = tz[mm][j];
+  if constexpr (PROD) {
+    if (tid == 0) prod_finish(a.hdr);  // every workgroup of the launch counts itself out
   }
 }
+
 
 // The pages' per-rank gate: for each token, t = the sum of its split
 // partials (rows 0..rank-1, split order), hidden = relu(W1 t + b1),
@@ -884,6 +1067,19 @@ static int ec_ksplit(int M, int K) {
   return ks < 1 ? 1 : ks;
 }
 
+// K splits of the compensator producers inside the GEMM launch (four waves
+// each): enough producer workgroups to keep about 256 busy, at most 8 splits
+// (a tile's epilogue reads every split of its sums) and at least 4 waves x 32
+// columns of K per split.
+static int fused_ksplit(int M, int K) {
+  const int nblk = (M + kEcTok - 1) / kEcTok;
+  int ks = (256 + nblk - 1) / nblk;
+  if (ks > 8) ks = 8;
+  const int cap = (K / 32) / 4;
+  if (ks > cap) ks = cap;
+  return ks < 1 ? 1 : ks;
+}
+
 // GEMM K splits: when the output has too few 128x128 tiles to fill the chip,
 // split K so that about kGemmSplitWgs workgroups run, each with at least 4
 // k-blocks and none empty.  ks * tiles <= kGemmSplitWgs bounds the partials.
@@ -1142,7 +1338,42 @@ hipError_t launch_prefill(const LayerDesc &L, int dtype, const uint16_t *x, uint
     return hipGetLastError();
   }
 
-  // concurrent: compensator on aux alongside the GEMM; U B^T after the join
+  if (!rgate && !split) {
+    // concurrent, scalar gate: the compensator's workgroups run inside the
+    // GEMM launch, ahead of its tiles (the aux stream is not needed)
+    const int nblk = (M + kEcTok - 1) / kEcTok;
+    const EcArgs ep{x, L.A, L.wg, L.K, M, L.rank, L.rank + 1, ea.rp1, fused_ksplit(M, L.K),
+                    (float *)(base + w.tp), nullptr, L.b_gate};
+    GemmArgs gf = g;
+    gf.nprod_real = nblk * ep.ks;
+    gf.nprod = (gf.nprod_real + 7) / 8 * 8;
+    gf.ntn = ggrid.x;
+    gf.ntm = ggrid.y;
+    gf.ec = ep;
+    gf.hdr = (WsHeader *)ws;
+    gf.spin_limit = get_decode_spin_limit();
+    gf.Tfb = (float *)(base + w.ts);
+    const dim3 fg(gf.nprod + gf.ntn * gf.ntm);
+    if (dtype == DT_F16) {
+      if (L.per_channel)
+        hipLaunchKernelGGL((prefill_gemm_kernel<DT_F16, true, true, false, true>), fg, dim3(256), 0,
+                           main_s, gf);
+      else
+        hipLaunchKernelGGL((prefill_gemm_kernel<DT_F16, false, true, false, true>), fg, dim3(256), 0,
+                           main_s, gf);
+    } else {
+      if (L.per_channel)
+        hipLaunchKernelGGL((prefill_gemm_kernel<DT_BF16, true, true, false, true>), fg, dim3(256), 0,
+                           main_s, gf);
+      else
+        hipLaunchKernelGGL((prefill_gemm_kernel<DT_BF16, false, true, false, true>), fg, dim3(256),
+                           0, main_s, gf);
+    }
+    return hipGetLastError();
+  }
+
+  // concurrent with the per-rank gate or a K-split GEMM: the compensator on
+  // the aux stream alongside the GEMM; U B^T after the join
   std::lock_guard<std::mutex> lock(g_event_mu);
   StreamEvents *evs = nullptr;
   if ((e = get_events(&evs)) != hipSuccess) return e;

@@ -73,18 +73,6 @@ struct WideArgs {
   int red_off;      // byte offset of the producers' wave sums in dynamic LDS
 };
 
-// Workgroup barrier for LDS only: this wave's LDS operations complete
-// (lgkmcnt(0)), then s_barrier.  __syncthreads() also carries a release fence
-// that waits for every outstanding global load (vmcnt(0)), which would drain
-// the weight and activation prefetches at every staged chunk.  The signal
-// fences keep the compiler from moving memory operations across.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // ---------------------------------------------------------------------------
 // Producers: one 16-row block of [A; w_g] over one K-split, for every token;
 // the sums go to tp[ksi][m][j].

@@ -624,6 +624,55 @@ def test_prefill_ragged_tail(N, K, G, r, M, dtype):
     assert_close(gpu_y_f64(y, dtype)[:, rows], oracle_y(hl, xb, rows=rows), f"tail {M} rows")
 
 
+FUSED_CASES = [
+    # N, K, G, r, M, dtype: unsplit GEMMs, scalar gate (the producers run inside the GEMM launch)
+    (300, 768, 128, 32, 200, "f16"),    # ragged N and M tiles
+    (384, 768, 256, 32, 257, "bf16"),   # G = 256, bf16, ragged M
+    (512, 512, 0, 16, 640, "f16"),      # per-channel, 5 token tiles
+    (256, 640, 128, 128, 150, "bf16"),  # the largest rank: 9 row blocks of [A; w_g]
+    (200, 512, 128, 100, 77, "f16"),    # rank 100: padded U rows
+]
+
+
+@pytest.mark.parametrize("N,K,G,r,M,dtype", FUSED_CASES)
+def test_prefill_concurrent_schedule(N, K, G, r, M, dtype):
+    """The concurrent schedule (compensator workgroups inside the GEMM launch, read by the
+    tiles' epilogues) and the serial one both match the oracle; the workspace counters the
+    concurrent launch uses are back at zero and no wait expired."""
+    note(f"prefill concurrent vs serial N={N} K={K} G={G} r={r} M={M} {dtype}")
+    hl, xb, lay, x = _setup(N, K, G, r, seed=N + K + M, dtype=dtype, M=M, outliers=True,
+                            b_gate=0.2)
+    ws = spear.new_workspace(lay, M)
+    assert spear.spear_linear_plan(lay, M, ws.numel(), "prefill")["k_splits"] == 1
+    y_ser = spear.spear_linear_prefill(lay, x, workspace=ws)
+    y_con = spear.spear_linear_prefill(lay, x, workspace=ws, aux_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    ref = oracle_y(hl, xb)
+    assert_close(gpu_y_f64(y_ser, dtype), ref, "serial")
+    assert_close(gpu_y_f64(y_con, dtype), ref, "concurrent")
+    assert spear.spear_workspace_flags(ws) == 0
+    assert _ws_header(ws) == [0] * 12
+
+
+@pytest.mark.parametrize("N,K,G,r,M,dtype", FUSED_CASES[:3])
+def test_prefill_concurrent_wait_expiry(N, K, G, r, M, dtype):
+    """With no wait for the producers (poll limit 0, set on the host), every GEMM tile of the
+    concurrent schedule computes the compensator sums of its tokens itself: the output still
+    matches the oracle, bit 0 of the workspace flags records the expiry, and the counters
+    are back at zero.  Every kernel exits normally."""
+    note(f"prefill concurrent, poll limit 0, N={N} K={K} r={r} M={M} {dtype}")
+    hl, xb, lay, x = _setup(N, K, G, r, seed=N + K + M + 1, dtype=dtype, M=M, outliers=True,
+                            b_gate=0.3)
+    with decode_spin_limit(0):
+        ws = spear.new_workspace(lay, M)
+        y = spear.spear_linear_prefill(lay, x, workspace=ws, aux_stream=torch.cuda.Stream())
+        torch.cuda.synchronize()
+    assert_close(gpu_y_f64(y, dtype), oracle_y(hl, xb), "self-computed sums")
+    assert spear.spear_workspace_flags(ws) & 1
+    hdr = _ws_header(ws)
+    assert hdr[0] == 0 and hdr[2:] == [0] * 10
+
+
 def test_prefill_gate_off_matches_rank_zero():
     note("prefill gate off")
     hl, xb, lay, x = _setup(256, 512, 128, 32, seed=11, M=96)
