@@ -684,6 +684,35 @@ def serving_context(torch, device):
     return out
 
 
+def serving_step(torch, device, steps=5):
+    """One step of the serving stack, for profiling: every linear of the 32-block stack at a
+    1024-token prefill chunk plus the 32 decode tokens, compensators on the configured 4
+    blocks, captured in one graph and replayed `steps` times; prints the step time."""
+    from quantized_gemm_error_amd import spear, synth
+    w = synth.WORKLOADS["llama7b-stack-serving"]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w["seed"])
+    shapes, n_dec, nb, C = list(w["shapes"]), w["decode_tokens"], w["blocks"], 1024
+    ecs = {int(b) for b in synth.ec_block_indices(nb, w["ec_blocks"], w["seed"])}
+    stack = [[random_layer(torch, N, K, w["group_size"], w["rank"], device, gen, torch.float16)
+              for K, N in shapes] for b in range(nb)]
+    stack = [[l if b in ecs else l.without_compensator() for l in blk] for b, blk in enumerate(stack)]
+    xs = {K: torch.randn((C, K), device=device, generator=gen).to(torch.float16) for K, _ in shapes}
+    ys = {N: torch.empty((C, N), dtype=torch.float16, device=device) for _, N in shapes}
+    # one workspace for every linear (the calls are ordered on one stream), sized for the largest
+    ws = spear.new_workspace(max((l for blk in stack for l in blk),
+                                 key=lambda l: spear.spear_workspace_bytes(l, C)), C)
+
+    def step(_i, s):
+        for blk in stack:
+            for si, (K, N) in enumerate(shapes):
+                spear.spear_linear(blk[si], xs[K][:C], y=ys[N][:C], workspace=ws, main_stream=s)
+                spear.spear_linear(blk[si], xs[K][:n_dec], y=ys[N][:n_dec], workspace=ws, main_stream=s)
+    t = graph_times_ms(torch, {"step": step}, 1, rounds=steps, warm_ms=0.0)["step"]
+    record_flags("serving", [ws])
+    return {"chunk": C, "decode_tokens": n_dec, "ec_blocks": sorted(ecs), "step_ms": round(t, 3)}
+
+
 def ceilings(torch, device):
     """Context only: a 1 GiB device-to-device copy, and hipBLASLt bf16 GEMMs at the prefill
     shapes (dense bf16 weights, torch.matmul)."""
@@ -816,7 +845,9 @@ def _is_dominant(name):
 
 
 def _short(name):
-    return name.replace("spear::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+    """A kernel's name without return type, namespaces and parameter list."""
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "").rsplit("(", 1)[0]
+    return n.replace("spear::w4::", "w4::").replace("spear::w8::", "w8::").replace("spear::", "")
 
 
 def measured_traffic():
@@ -957,6 +988,71 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir):
     print(json.dumps(rec))
 
 
+LAYER_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_{tag}_trace -o run -- python3 bench.py {mode}",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_{tag}_fetch -o run -- python3 bench.py {mode} --copy-calibration",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_{tag}_write -o run -- python3 bench.py {mode} --copy-calibration",
+}
+LAYER_MODES = {"llama70b_layer": "--llama70b-only", "serving_step_7b": "--serving-step"}
+
+
+def summarize_layer_profiles(tag, title, trace_dir, fetch_dir, write_dir, out_dir):
+    """Per (kernel, grid size): dispatches, mean duration (trace run) and mean HBM bytes read
+    and written per dispatch (FETCH_SIZE and WRITE_SIZE runs, each scaled by what the same
+    counter reads for a device-to-device copy of known size)."""
+    import csv
+    import statistics
+
+    def rows(path):
+        with open(path, newline="") as f:
+            return list(csv.DictReader(f))
+
+    trace = rows(os.path.join(trace_dir, "run_kernel_trace.csv"))
+    dur = {}
+    for r in trace:
+        if r["Kernel_Name"].startswith("__amd_rocclr") or "at::" in r["Kernel_Name"]:
+            continue   # copies and the set-up's torch kernels
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        key = (_short(r["Kernel_Name"]), grid)
+        dur.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def counter_pass(d):
+        rs = rows(os.path.join(d, "run_counter_collection.csv"))
+        rs.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = [r for r in rs if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")][-3:]
+        cal = statistics.mean(float(r["Counter_Value"]) for r in copies)
+        scale = cal / (COPY_CAL_BYTES / 1024.0)
+        per = {}
+        for r in rs:
+            if r["Kernel_Name"].startswith("__amd_rocclr"):
+                continue
+            per.setdefault((_short(r["Kernel_Name"]), int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return scale, cal, {k: statistics.mean(v) * 1024.0 / scale for k, v in per.items()}
+
+    f_scale, f_cal, fetch = counter_pass(fetch_dir)
+    w_scale, w_cal, write = counter_pass(write_dir)
+    mode = LAYER_MODES.get(tag, "")
+    lines = [f"# {title}: rocprofv3 trace and HBM traffic", "",
+             "Commands (repository root, one MI355X; counters one per pass):", ""]
+    lines += ["    " + LAYER_CMDS[k].format(tag=tag, mode=mode) for k in ("trace", "fetch", "write")]
+    lines += ["", f"Byte scale: the last three dispatches of each counter pass copy {COPY_CAL_BYTES >> 20} "
+                  f"MiB device to device; FETCH_SIZE reads {f_cal:.1f} KiB (scale {f_scale:.5f}), "
+                  f"WRITE_SIZE {w_cal:.1f} KiB (scale {w_scale:.5f}) per copy.", "",
+              "rocprofv3 stamps a kernel's start when the previous one in the stream ends, so "
+              "back-to-back durations are launch to launch.", "",
+              "| kernel | grid (threads) | dispatches | mean us | read MB | written MB | GB/s (read+written) |",
+              "|---|---:|---:|---:|---:|---:|---:|"]
+    for key in sorted(dur, key=lambda k: -statistics.mean(dur[k]) * len(dur[k])):
+        d = statistics.mean(dur[key])
+        fb, wb = fetch.get(key), write.get(key)
+        rate = f"{(fb + wb) / (d * 1e-6) / 1e9:.0f}" if fb is not None and wb is not None and d > 0 else "-"
+        lines.append(f"| `{key[0][:80]}` | {key[1]} | {len(dur[key])} | {d:.2f} | "
+                     f"{'-' if fb is None else f'{fb / 1e6:.3f}'} | {'-' if wb is None else f'{wb / 1e6:.3f}'} | {rate} |")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"{tag}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 PREFILL_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_prefill_trace -o run -- "
                      "python3 bench.py --prefill-only")
 PREFILL_PMC = (("pmc1", "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
@@ -1065,6 +1161,15 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the Llama-7B prefill calls (M = 2048, bf16) and print them: "
                          "the command that the prefill kernel profiles are taken with")
+    ap.add_argument("--llama70b-only", action="store_true",
+                    help="run only the Llama-70B layer leg and print it (profiling)")
+    ap.add_argument("--serving-step", action="store_true",
+                    help="replay one serving step (32 blocks x 3 linears, 1024-token chunk + 32 "
+                         "decode tokens) a few times and print its time (profiling)")
+    ap.add_argument("--summarize-layer-profiles", nargs=5,
+                    metavar=("TAG", "TITLE", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/TAG.md: per kernel and grid, duration and copy-scaled "
+                         "HBM bytes from rocprofv3 CSV output (no GPU)")
     ap.add_argument("--serving-only", action="store_true",
                     help="run only the serving-stack leg (latency table, chunk selector, request "
                          "stream) and print it")
@@ -1074,6 +1179,9 @@ def main():
         return
     if args.summarize_prefill_profiles:
         summarize_prefill_profiles(*args.summarize_prefill_profiles, out_dir=os.path.join(ROOT, "profiles"))
+        return
+    if args.summarize_layer_profiles:
+        summarize_layer_profiles(*args.summarize_layer_profiles, out_dir=os.path.join(ROOT, "profiles"))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path "
@@ -1092,6 +1200,17 @@ def main():
         return
     if args.serving_only:
         print(json.dumps({"serving_stack_7b": serving_context(torch, dev)}), flush=True)
+        return
+    if args.llama70b_only or args.serving_step:
+        out = ({"llama70b_layer_fp16": llama70b_context(torch, dev)} if args.llama70b_only
+               else {"serving_step": serving_step(torch, dev)})
+        if args.copy_calibration:   # the reference copies that scale the byte counters
+            src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps(out), flush=True)
         return
 
     log("building decode workload")

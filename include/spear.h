@@ -225,14 +225,23 @@ spear_status_t spear_linear_decode_noalloc(const spear_layer_t *layer, spear_dty
                                            spear_stream_t stream);
 
 /*
- * Prefill path (2.2 A, prefill phase): any M >= 1.  The 4-bit product runs on
- * main_stream as an MFMA GEMM over LDS-staged dequantized tiles; the
- * compensator's thin products (gate, A x, scaled by the gate) run on
- * aux_stream concurrently, and main_stream joins aux_stream before the
- * gated B (A x) term is added to y.  aux_stream == NULL (or equal to
- * main_stream) runs everything in order on main_stream.  When the call
- * returns, work on aux_stream is ordered after main_stream's prior work and
- * main_stream's later work is ordered after all of it.
+ * Prefill path (2.2 A, prefill phase): any M >= 1.  The 4-bit product is an
+ * MFMA GEMM over LDS-staged dequantized tiles; the compensator's thin
+ * products (gate, A x, scaled by the gate) are added in the GEMM tiles'
+ * epilogue before y is rounded once.  Two schedules:
+ *   aux_stream == NULL (or equal to main_stream): serial, all on main_stream:
+ *     the compensator kernels, then the GEMM.
+ *   aux_stream given: concurrent.  With the scalar gate and an unsplit GEMM
+ *     (enough 128x128 output tiles), the compensator runs as producer
+ *     workgroups inside the GEMM launch on main_stream, dispatched ahead of
+ *     the tiles; each tile waits for them (bounded by the decode spin limit,
+ *     see spear_set_decode_spin_limit) before its epilogue and computes the
+ *     sums of its own tokens if the wait expires (bit 0 of the workspace
+ *     flags).  aux_stream is then not used.  Otherwise (per-rank gate, or a
+ *     K-split GEMM at few tiles) the compensator kernels run on aux_stream
+ *     beside the GEMM and a finish kernel adds their term after the join.
+ * When the call returns, work on aux_stream is ordered after main_stream's
+ * prior work and main_stream's later work is ordered after all of it.
  */
 spear_status_t spear_linear_prefill(const spear_layer_t *layer, spear_dtype_t dtype,
                                     const void *x, void *y, int32_t M, void *workspace,

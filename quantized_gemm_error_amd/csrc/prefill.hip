@@ -21,19 +21,26 @@
 //    several workgroups that store fp32 partial tiles;
 //  * prefill_finish_kernel completes 64x64 output tiles: the sum of the GEMM's
 //    split partials (with the per-channel scale) or the rounded y of the
-//    concurrent schedule, plus U B^T, rounded once into y.
-//
-// Every reduction across workgroups happens across a kernel boundary, so no
-// kernel here waits on another workgroup.
+//    two-stream concurrent schedule, plus U B^T, rounded once into y.
 //
 // Schedules:
 //  * serial (no aux stream): compensator, then the GEMM, whose epilogue adds
 //    U B^T before y is rounded once (or, with K split, the finish kernel
-//    does).  On MI355X this is the faster order: the GEMM's workgroups fill
-//    every CU, so a kernel on another stream only runs as they retire;
-//  * concurrent (aux stream given, the pages' schedule): the compensator on
-//    the aux stream alongside the GEMM on the main stream; after the join the
-//    finish kernel adds U B^T.
+//    does).  Every reduction across workgroups happens across a kernel
+//    boundary;
+//  * concurrent (aux stream given, the pages' overlap of the compensator with
+//    the GEMM).  A kernel on a second stream gets no CU while the GEMM's
+//    workgroups fill every CU, so on MI355X the overlap happens inside one
+//    launch: its first workgroups are compensator producers (ec_block, four
+//    waves each), dispatched ahead of the GEMM tiles; they publish their
+//    K-split sums with agent-scope stores and count themselves in, and each
+//    tile's epilogue, after a bounded wait for that count, forms its U rows
+//    from the sums exactly as prefill_u_kernel does (or, if the wait
+//    expires, computes its tokens' sums itself) and adds U B^T before y is
+//    rounded once.  The last workgroup to finish resets the counters.  With
+//    the per-rank gate or a K-split GEMM the compensator kernels run on the
+//    aux stream beside the GEMM, and after the join the finish kernel adds
+//    U B^T.
 #include <algorithm>
 #include <mutex>
 #include <unordered_map>
