@@ -30,6 +30,7 @@
 // count its loads exactly.
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -43,6 +44,19 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kCb = 4;               // 128-wide blocks per staged x chunk (= ring depth)
 constexpr int kChunkCols = 128 * kCb;
 constexpr int kXStr = kChunkCols + 8;  // LDS row stride of a staged chunk (halves)
+
+// Place of 16-byte piece p (of 64) within a staged row: bits 2 and 4 of p
+// swapped.  Piece p = 16 i + 4 h + t is what lane (token m, quarter h) reads
+// for block i, step t.  With the row stride of 65 pieces, that read falls in
+// bank group (m + place(p)) mod 32 of the 32 groups of 16 bytes; one pass of
+// a 16-byte LDS read serves 32 lanes, quarters h and h + 1 of all 16 tokens,
+// and the swap puts those two quarters 16 groups apart, so the pass touches
+// 32 distinct groups (in natural order quarter h + 1 landed 4 groups on, and
+// 12 of its 16 lanes met a lane of quarter h).  The place is additive over
+// the fields of p, so every read keeps a compile-time offset.
+__host__ __device__ constexpr int xplace(int p) {
+  return (p & 0x2B) | ((p >> 2) & 1) << 4 | ((p >> 4) & 1) << 2;
+}
 constexpr int kMaxLds = 160 * 1024;
 // Launch-shape constants of plan_wide (measured on MI355X).
 #ifndef SPEAR_WIDE_R64
@@ -145,12 +159,18 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   const int lane = tid & 63, col = lane & 15, h = lane >> 4;
   const int q = c % a.ksp, tile = c / a.ksp;
   const int n0 = tile * 16 * R * kWaves;
+  // each wave's 16-row blocks of packed weights as buffer resources of one
+  // block each (2 K words): tile kb of the block is 1 KB at kb * 1024, and a
+  // lane's piece of a tile past K reads as zeros through the range check
+  // (the staged x is zero there).  Rows past N repeat the last block.
   int row[R];
-  const uint32_t *wblk[R];
+  __amdgpu_buffer_rsrc_t wrs[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     row[r] = min(n0 + 16 * (wave * R + r) + col, a.N - 1);
-    wblk[r] = tiled_block(a.qw, n0 + 16 * (wave * R + r), a.N, a.K, lane);
+    const int rb = min(n0 + 16 * (wave * R + r), a.N - 1) >> 4;
+    wrs[r] = __builtin_amdgcn_make_buffer_rsrc((void *)(a.qw + (size_t)rb * 2 * a.K), (short)0,
+                                               a.K * 8, 0x00020000);
   }
   const int kb0 = q * a.nbs;                 // the plan leaves no split empty
   const int nbl = min(a.nb, kb0 + a.nbs) - kb0;
@@ -188,15 +208,21 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
       xr[i] = *(const u32x4_t *)(a.x + (size_t)m * a.K + k);
     }
   };
-  // (the zero fill is a bit mask, so that the loop body stays one basic block)
-  auto xstore = [&](int g) {
+  // Only the split's last group reaches past its end (or past K): its
+  // columns there are staged as zeros, through a bit mask.  Rows past M hold
+  // copies of row M - 1 (xload clamps), which no kept output reads.
+  auto xstore = [&](int g, auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
       const int p = tid + kThreads * i;
       const int m = p >> 6, j = p & 63;
-      const uint32_t keep = (m < a.M && kx0 + g * kChunkCols + 8 * j < kend) ? ~0u : 0u;
-      const u32x4_t v = {xr[i][0] & keep, xr[i][1] & keep, xr[i][2] & keep, xr[i][3] & keep};
-      *(u32x4_t *)(lds + m * kXStr + 8 * j) = permute_8(v);
+      u32x4_t v = xr[i];
+      if constexpr (kMask) {
+        const uint32_t keep = (kx0 + g * kChunkCols + 8 * j < kend) ? ~0u : 0u;
+        v = u32x4_t{v[0] & keep, v[1] & keep, v[2] & keep, v[3] & keep};
+      }
+      *(u32x4_t *)(lds + m * kXStr + 8 * xplace(j)) = permute_8(v);
     }
   };
 
@@ -209,9 +235,8 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   uint32_t sr[D][R], zr[D][R];
   auto wload = [&](int b, int r, u32x4_t &w, uint32_t &sv, uint32_t &zv) {
     const int kb = kb0 + min(b, nbl - 1);
-    // (a piece past K reads the block's first piece instead)
-    const int off = (kb * 128 + 32 * h < a.K) ? kb * 256 : -4 * lane;
-    w = __builtin_nontemporal_load((const u32x4_t *)(wblk[r] + off));
+    // read once per call: non-temporal
+    w = __builtin_amdgcn_raw_buffer_load_b128(wrs[r], 16 * lane, kb * 1024, 2);
     if constexpr (!PERCH) {
       const int g = (kb * 128) / a.G;
       const size_t e = (size_t)row[r] * a.ngroups + g;
@@ -247,9 +272,9 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   // refill issues would take a register copy at the loop's back edge, and
   // that copy waits for the load, draining the ring every group.
   const int ngr = (nbl + D - 1) / D;
-  for (int g = 0; g < ngr; ++g) {
+  auto run_group = [&](int g, auto mask_tag) {
     lds_barrier();  // every wave is done with group g - 1's chunk
-    xstore(g);
+    xstore(g, mask_tag);
     lds_barrier();
     xload(g + 1);     // clamped: past the split it reloads valid columns, staged as zeros
     // keep the prefetches here: the scheduler would otherwise move loads whose
@@ -275,7 +300,7 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
 #pragma unroll
       for (int r = 0; r < R; ++r) wload(b + D, r, ring[i][r], sr[i][r], zr[i][r]);
       __builtin_amdgcn_sched_barrier(0);
-      const uint16_t *xb = lds + i * 128 + 32 * h;
+      const uint16_t *xb = lds + 8 * (xplace(16 * i) + xplace(4 * h));
       f32x4_t gacc[R][MB];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -302,7 +327,10 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
           for (int mb = 0; mb < MB; ++mb) acc[r][mb] += sc[r] * gacc[r][mb];
       }
     }
-  }
+  };
+  // every group but the last as one loop of straight-line code, then the last
+  for (int g = 0; g + 1 < ngr; ++g) run_group(g, std::false_type{});
+  run_group(ngr - 1, std::true_type{});
   if constexpr (PERCH) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
