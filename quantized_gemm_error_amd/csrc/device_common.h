@@ -59,6 +59,22 @@ __device__ __forceinline__ const uint32_t *tiled_block(const uint32_t *qw, int n
   return qw + (size_t)rb * 2 * K + 4 * lane;
 }
 
+// The same block as a buffer resource of its 2 K words (n_block uniform
+// across the wave): tile kb of it is 1 KB at byte kb * 1024, a lane's piece
+// at 16 lane bytes into the tile (tile_piece).  A piece past K lies past the
+// block's end and reads as zeros through the range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tiled_block_rsrc(const uint32_t *qw, int n_block,
+                                                                   int N, int K) {
+  const int rb = min(n_block, N - 1) >> 4;
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(qw + (size_t)rb * 2 * K), (short)0, K * 8,
+                                           0x00020000);
+}
+
+// A lane's 16-byte piece of tile kb, read once per call (non-temporal).
+__device__ __forceinline__ u32x4_t tile_piece(__amdgpu_buffer_rsrc_t blk, int kb, int lane) {
+  return __builtin_amdgcn_raw_buffer_load_b128(blk, 16 * lane, kb * 1024, 2);
+}
+
 // Workgroup barrier for LDS only: this wave's LDS operations complete
 // (lgkmcnt(0)), then s_barrier.  __syncthreads() also carries a release fence
 // that waits for every outstanding global load (vmcnt(0)), which would drain

@@ -159,18 +159,15 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   const int lane = tid & 63, col = lane & 15, h = lane >> 4;
   const int q = c % a.ksp, tile = c / a.ksp;
   const int n0 = tile * 16 * R * kWaves;
-  // each wave's 16-row blocks of packed weights as buffer resources of one
-  // block each (2 K words): tile kb of the block is 1 KB at kb * 1024, and a
-  // lane's piece of a tile past K reads as zeros through the range check
-  // (the staged x is zero there).  Rows past N repeat the last block.
+  // each wave's 16-row blocks of packed weights as buffer resources (a
+  // lane's piece of a tile past K reads as zeros; the staged x is zero there
+  // too).  Rows past N repeat the last block.
   int row[R];
   __amdgpu_buffer_rsrc_t wrs[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     row[r] = min(n0 + 16 * (wave * R + r) + col, a.N - 1);
-    const int rb = min(n0 + 16 * (wave * R + r), a.N - 1) >> 4;
-    wrs[r] = __builtin_amdgcn_make_buffer_rsrc((void *)(a.qw + (size_t)rb * 2 * a.K), (short)0,
-                                               a.K * 8, 0x00020000);
+    wrs[r] = tiled_block_rsrc(a.qw, n0 + 16 * (wave * R + r), a.N, a.K);
   }
   const int kb0 = q * a.nbs;                 // the plan leaves no split empty
   const int nbl = min(a.nb, kb0 + a.nbs) - kb0;
@@ -235,8 +232,7 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   uint32_t sr[D][R], zr[D][R];
   auto wload = [&](int b, int r, u32x4_t &w, uint32_t &sv, uint32_t &zv) {
     const int kb = kb0 + min(b, nbl - 1);
-    // read once per call: non-temporal
-    w = __builtin_amdgcn_raw_buffer_load_b128(wrs[r], 16 * lane, kb * 1024, 2);
+    w = tile_piece(wrs[r], kb, lane);
     if constexpr (!PERCH) {
       const int g = (kb * 128) / a.G;
       const size_t e = (size_t)row[r] * a.ngroups + g;
