@@ -250,7 +250,14 @@ spear_status_t spear_linear_prefill(const spear_layer_t *layer, spear_dtype_t dt
 
 /*
  * Phase-aware dispatch (2.2 A): M <= spear_get_decode_max_m() goes to the
- * decode path on main_stream, larger M to the prefill path.
+ * decode path on main_stream, larger M to the prefill path.  One mixed case
+ * is split: when the prefill's last 128-token tile row would hold only
+ * r = M mod 128 <= 32 tokens after at least 8 full tile rows (a prefill
+ * chunk with a few decode tokens appended), the first M - r tokens take the
+ * prefill path and the last r the decode path, one after the other on
+ * main_stream (r must also be within the decode threshold, and the
+ * workspace large enough for both; spear_workspace_bytes(layer, M) is).
+ * Every argument is validated before anything is launched.
  */
 spear_status_t spear_linear(const spear_layer_t *layer, spear_dtype_t dtype, const void *x,
                             void *y, int32_t M, void *workspace, size_t workspace_bytes,
@@ -344,7 +351,9 @@ typedef enum spear_path {
   SPEAR_PATH_DECODE = 1,        /* fused decode, one workgroup per group of output rows */
   SPEAR_PATH_DECODE_SPLIT = 2,  /* fused decode, K split across each 128-row tile's workgroups */
   SPEAR_PATH_PREFILL = 3,       /* the prefill GEMM path */
-  SPEAR_PATH_DECODE_WIDE = 4    /* fused decode for 33..128 tokens: 256-row tiles over K-splits */
+  SPEAR_PATH_DECODE_WIDE = 4,   /* fused decode for 33..128 tokens: 128-row tiles over K-splits */
+  SPEAR_PATH_PREFILL_DECODE_TAIL = 5 /* spear_linear only: prefill for M - r tokens, then decode for
+                                        the last r (the plan describes the prefill launch) */
 } spear_path_t;
 
 typedef struct spear_plan {

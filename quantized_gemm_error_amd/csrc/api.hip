@@ -140,6 +140,16 @@ bool decode_fits(const LayerDesc &d, int M) {
 size_t decode_need(const LayerDesc &d, int M) {
   return M <= kSmallDecodeM ? decode_workspace_bytes(d, M) : wide_workspace_bytes(d, M);
 }
+
+// The decode tail of a prefill-sized call (prefill_decode_tail), when the
+// decode path takes those tokens with this workspace; 0 otherwise.
+int dispatch_decode_tail(const LayerDesc &d, int M, void *workspace, size_t workspace_bytes) {
+  const int r = prefill_decode_tail(M);
+  if (r == 0 || r > g_decode_max_m.load() || !decode_fits(d, r)) return 0;
+  const size_t need = decode_need(d, r);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return 0;
+  return r;
+}
 hipError_t decode_launch(const LayerDesc &d, int dtype, const void *x, void *y, int M, void *ws,
                          size_t ws_bytes, hipStream_t s) {
   if (M <= kSmallDecodeM)
@@ -306,8 +316,23 @@ spear_status_t spear_linear(const spear_layer_t *layer, spear_dtype_t dtype, con
                             spear_stream_t main_stream, spear_stream_t aux_stream) {
   if (M >= 0 && M <= g_decode_max_m.load())
     return spear_linear_decode(layer, dtype, x, y, M, workspace, workspace_bytes, main_stream);
-  return spear_linear_prefill(layer, dtype, x, y, M, workspace, workspace_bytes, main_stream,
-                              aux_stream);
+  // a call whose last tile row holds few tokens: the prefill path for the
+  // tokens before it, then the decode path for those few, both on
+  // main_stream (rows are independent); everything is validated first
+  LayerDesc d;
+  int r = 0;
+  if (M > 0 && check_layer(layer, &d) == SPEAR_OK && check_io(dtype, x, y) == SPEAR_OK)
+    r = dispatch_decode_tail(d, M, workspace, workspace_bytes);
+  if (r == 0)
+    return spear_linear_prefill(layer, dtype, x, y, M, workspace, workspace_bytes, main_stream,
+                                aux_stream);
+  const int m0 = M - r;
+  spear_status_t st = spear_linear_prefill(layer, dtype, x, y, m0, workspace, workspace_bytes,
+                                           main_stream, aux_stream);
+  if (st != SPEAR_OK) return st;
+  return spear_linear_decode(layer, dtype, (const char *)x + (size_t)m0 * d.K * 2,
+                             (char *)y + (size_t)m0 * d.N * 2, r, workspace, workspace_bytes,
+                             main_stream);
 }
 
 spear_status_t spear_linear_plan(const spear_layer_t *layer, int32_t M, size_t workspace_bytes,
@@ -339,7 +364,9 @@ spear_status_t spear_linear_plan(const spear_layer_t *layer, int32_t M, size_t w
     if ((ws || prefill_needs_workspace(d)) &&
         (st = check_ws(ws, workspace_bytes, prefill_workspace_bytes(d, M))) != SPEAR_OK)
       return st;
-    describe_prefill(d, M, workspace_bytes, plan);
+    const int r = phase == 0 ? dispatch_decode_tail(d, M, ws, workspace_bytes) : 0;
+    describe_prefill(d, M - r, workspace_bytes, plan);
+    if (r > 0) plan->path = SPEAR_PATH_PREFILL_DECODE_TAIL;
   }
   return ok();
 }

@@ -126,6 +126,7 @@ void describe_decode(const LayerDesc &L, int M, size_t ws_bytes, spear_plan_t *o
 void describe_prefill(const LayerDesc &L, int M, size_t ws_bytes, spear_plan_t *out);
 size_t prefill_workspace_bytes(const LayerDesc &L, int M);
 bool prefill_needs_workspace(const LayerDesc &L);  // false: optional (splits K when given)
+int prefill_decode_tail(int M);  // tokens of an M-token call the dispatch gives to decode (0: none)
 
 // prefill.hip kernels shared with the wide decode launch
 hipError_t launch_form_u(const LayerDesc &L, const float *Tp, int ks, int M, float *U,

@@ -1171,6 +1171,22 @@ size_t prefill_workspace_bytes(const LayerDesc &L, int M) { return prefill_ws_la
 
 bool prefill_needs_workspace(const LayerDesc &L) { return L.rank > 0; }
 
+// Tokens at the end of an M-token call that the phase-aware dispatch hands
+// to the decode path: the r = M mod BM tokens of a last, partly filled tile
+// row, when r <= kDecodeTailMax and at least kDecodeTailRows full tile rows
+// come before them.  That tile row costs the GEMM a whole row of 128-token
+// tiles (a ninth, at eight full rows) for r tokens, while the fused decode
+// handles r <= 32 tokens in about the time of streaming the weights once;
+// measured on the serving stack's merged batches (a 1024-token chunk plus 32
+// decode tokens: 13.3 ms a step in one GEMM, 11.6 ms in two calls), while at
+// 256 and 512 tokens the single GEMM stays ahead.  0: no split.
+constexpr int kDecodeTailMax = 32;
+constexpr int kDecodeTailRows = 8;
+int prefill_decode_tail(int M) {
+  const int r = M % BM;
+  return (r >= 1 && r <= kDecodeTailMax && M - r >= kDecodeTailRows * BM) ? r : 0;
+}
+
 void describe_prefill(const LayerDesc &L, int M, size_t ws_bytes, spear_plan_t *out) {
   const int gks = ws_bytes > 0 ? gemm_ksplit(M, L.N, L.K) : 1;
   const int tail = (ws_bytes > 0 && gks == 1) ? prefill_tail_rows(M, L.N, L.K) : 0;

@@ -43,7 +43,8 @@ SPEAR_PATH_DECODE = 1
 SPEAR_PATH_DECODE_SPLIT = 2
 SPEAR_PATH_PREFILL = 3
 SPEAR_PATH_DECODE_WIDE = 4
-PATH_NAMES = {0: "none", 1: "decode", 2: "decode_split", 3: "prefill", 4: "decode_wide"}
+PATH_NAMES = {0: "none", 1: "decode", 2: "decode_split", 3: "prefill", 4: "decode_wide",
+              5: "prefill_decode_tail"}
 
 
 class SpearError(RuntimeError):

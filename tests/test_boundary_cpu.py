@@ -274,6 +274,30 @@ def test_plan_dispatch_and_errors(lib):
     assert _plan(lay0, 100, 0)["workspace_bytes"] == 0
 
 
+def test_dispatch_splits_off_a_short_decode_tail(lib):
+    """spear_linear gives the last r = M mod 128 tokens to the decode path when 1 <= r <= 32,
+    at least eight full 128-token tile rows precede them, r is within the decode threshold
+    and the workspace holds the decode call's needs; the plan then describes the prefill
+    launch for the first M - r tokens."""
+    lay = _layer(N=4096, K=4096, group_size=128, rank=32)
+    ws = lib.spear_workspace_bytes(ctypes.byref(lay), 2080)
+    for M, tail in ((1056, 32), (1025, 1), (2080, 32), (2048 + 17, 17), (1024, 0), (1064, 0),
+                    (288, 0), (544, 0), (1023, 0), (900, 0)):
+        plan = _plan(lay, M, ws)
+        assert plan["path"] == ("prefill_decode_tail" if tail else "prefill"), (M, plan)
+        assert plan == dict(_plan(lay, M - tail, ws, "prefill"), path=plan["path"]), M
+        assert _plan(lay, M, ws, "prefill")["path"] == "prefill"   # explicit prefill: never split
+    old = spear.spear_get_decode_max_m()
+    try:
+        spear.spear_set_decode_max_m(16)                    # the tail must be a decode-sized M
+        assert _plan(lay, 1056, ws)["path"] == "prefill"
+        assert _plan(lay, 1040, ws)["path"] == "prefill_decode_tail"
+    finally:
+        spear.spear_set_decode_max_m(old)
+    lay0 = _layer(N=4096, K=4096, group_size=128, rank=0, A=None, B=None, w_gate=None)
+    assert _plan(lay0, 1056, 0)["path"] == "prefill_decode_tail"   # rank 0: no workspace needed
+
+
 def test_workspace_holds_only_the_partials_a_call_can_split_into(lib):
     """Decode-sized workspaces carry no 32 MiB of GEMM partials: at M <= 32 the prefill
     split partials are at most ks * 32 * N * 4 bytes."""

@@ -35,7 +35,12 @@ def test_serving_shapes_fp16_prefill(K, N):
     aux = torch.cuda.Stream()
     for C in W["chunks"]:
         for M in (C, C + W["decode_tokens"]):
-            toks = np.unique(np.r_[np.random.default_rng(M).choice(M, 40, replace=False), 0, M - 1])
+            # the last tokens too: past 1024 the dispatch gives the last 32 to the decode path
+            toks = np.unique(np.r_[np.random.default_rng(M).choice(M, 40, replace=False), 0,
+                                   M - 1 - np.arange(0, 32, 5)])
+            path = spear.spear_linear_plan(lay, M, ws.numel())["path"]
+            assert path == ("prefill_decode_tail" if M == C + W["decode_tokens"] and C >= 1024
+                            else "prefill"), (M, path)
             ref = oracle_y(hl, xb[toks], rows=rows)
             for schedule in ("serial", "concurrent"):
                 note(f"serving fp16 prefill K={K} N={N} M={M} {schedule}")

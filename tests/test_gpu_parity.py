@@ -711,6 +711,33 @@ def test_decode_and_prefill_agree_and_dispatch():
     assert torch.equal(yl80.view(torch.int16), yp80.view(torch.int16))   # M = 80 -> prefill
 
 
+@pytest.mark.parametrize("dtype,M,rank", [("f16", 1024 + 32, 32), ("bf16", 1024 + 7, 16),
+                                           ("f16", 1152 + 1, 0)])
+def test_dispatch_decode_tail(dtype, M, rank):
+    """spear_linear past 1024 tokens with a last tile row of r <= 32 tokens: the prefill path
+    for the first M - r tokens and the decode path for the last r.  The whole output matches
+    the oracle, and each part is bitwise the explicit call on its rows (serial and with the
+    aux stream)."""
+    note(f"dispatch decode tail {dtype} M={M} r={rank}")
+    r = M % 128
+    hl, xb, lay, x = _setup(200, 512, 128, rank, seed=41 + M, dtype=dtype, M=M, outliers=True)
+    ws = spear.new_workspace(lay, M)
+    assert spear.spear_linear_plan(lay, M, ws.numel())["path"] == "prefill_decode_tail"
+    ref = oracle_y(hl, xb)
+    aux = torch.cuda.Stream()
+    y = spear.spear_linear(lay, x, workspace=ws)
+    ya = spear.spear_linear(lay, x, workspace=ws, aux_stream=aux)
+    head = spear.spear_linear_prefill(lay, x[:M - r].contiguous(), workspace=ws)
+    tail = spear.spear_linear_decode(lay, x[M - r:].contiguous(), workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(gpu_y_f64(y, dtype), ref, f"tail split {dtype} M={M}")
+    assert_close(gpu_y_f64(ya, dtype), ref, f"tail split, aux stream {dtype} M={M}")
+    assert torch.equal(y[:M - r].view(torch.int16), head.view(torch.int16))
+    assert torch.equal(y[M - r:].view(torch.int16), tail.view(torch.int16))
+    assert spear.spear_workspace_flags(ws) == 0
+    assert _ws_header(ws) == [0] * 12
+
+
 def test_prefill_rank0_split_k_with_and_without_workspace():
     """Rank 0: with a workspace the GEMM splits K (2 output tiles, 8 splits), without one
     it does not; both match the oracle and each other within the tolerance."""
