@@ -193,18 +193,20 @@ def test_decode_soak_graph_replayed():
 
 def test_library_graph_of_layer_calls():
     """The library's own static graph (spear_graph_*): a prefill call whose compensator runs
-    on the graph's aux branch, a decode call and a second prefill call sharing the decode
-    call's workspace, captured once and launched 100 times; every launch equals the eager
-    calls (the same schedule: prefill with an aux stream) bit for bit."""
+    on the graph's aux branch, a decode call, a second prefill call sharing the decode call's
+    workspace, and a 1031-token call that the dispatch splits (prefill for 1024 tokens, decode
+    for the last 7), captured once and launched 100 times; every launch equals the eager calls
+    (the same schedule: prefill with an aux stream) bit for bit."""
     specs = [(1024, 4096, 128, 32, 512), (2048, 1024, 0, 16, 4), (2048, 1024, 0, 16, 200)]
     hl1 = synth.make_layer(1024, 4096, 128, 32, seed=31, b_gate=0.1)
     hl2 = synth.make_layer(2048, 1024, 0, 16, seed=32, b_gate=-0.2)
     l1, l2 = spear.layer_to_device(hl1, DEV), spear.layer_to_device(hl2, DEV)
-    ws1, ws2 = spear.new_workspace(l1, 512), spear.new_workspace(l2, 200)
-    xb1 = synth.make_activations(512, 4096, seed=33, outliers=True)
+    ws1, ws2 = spear.new_workspace(l1, 1031), spear.new_workspace(l2, 200)
+    xb1 = synth.make_activations(1031, 4096, seed=33, outliers=True)
     xb2 = synth.make_activations(200, 1024, seed=34, outliers=True)
     x1, x2 = spear.act_to_device(xb1, "f16", DEV), spear.act_to_device(xb2, "f16", DEV)
-    calls = [(l1, x1, ws1), (l2, x2[:4], ws2), (l2, x2, ws2)]
+    assert spear.spear_linear_plan(l1, 1031, ws1.numel())["path"] == "prefill_decode_tail"
+    calls = [(l1, x1[:512], ws1), (l2, x2[:4], ws2), (l2, x2, ws2), (l1, x1, ws1)]
     outs = [torch.empty((x.shape[0], lay.N), dtype=torch.float16, device=DEV) for lay, x, _ in calls]
     stream, aux = torch.cuda.Stream(), torch.cuda.Stream()
     note("library graph eager")
@@ -213,7 +215,8 @@ def test_library_graph_of_layer_calls():
             spear.spear_linear(lay, x, y=y, workspace=ws, main_stream=stream, aux_stream=aux)
     torch.cuda.synchronize()
     refs = [o.clone() for o in outs]
-    for (hl, xb, M), r in zip([(hl1, xb1, 512), (hl2, xb2, 4), (hl2, xb2, 200)], refs):
+    for (hl, xb, M), r in zip([(hl1, xb1, 512), (hl2, xb2, 4), (hl2, xb2, 200), (hl1, xb1, 1031)],
+                              refs):
         rows = sample_rows(hl.N, 64, seed=M)
         toks = np.unique(np.r_[np.random.default_rng(M).choice(M, min(M, 24), replace=False), M - 1])
         assert_close(gpu_y_f64(r, "f16")[np.ix_(toks, rows)], oracle_y(hl, xb[:M][toks], rows=rows),
@@ -233,4 +236,5 @@ def test_library_graph_of_layer_calls():
     _replay_and_check(_Replay(), outs, refs, 100,
                       lambda: _eager_noise(l2, x2[:3], ws2), stream)
     assert spear.spear_workspace_flags(ws2) == 0 and _header_zero(ws2)
+    assert spear.spear_workspace_flags(ws1) == 0 and _header_zero(ws1)
     g.destroy()
