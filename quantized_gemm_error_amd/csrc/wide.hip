@@ -68,6 +68,20 @@ constexpr int kMaxLds = 160 * 1024;
 #ifndef SPEAR_WIDE_MAX_KSP
 #define SPEAR_WIDE_MAX_KSP 16
 #endif
+#ifndef SPEAR_WIDE_LOOKAHEAD
+#define SPEAR_WIDE_LOOKAHEAD 2  // steps by which the x-fragment reads run ahead of their MFMAs
+#endif
+// The same at 128 tokens, where 0 leaves the order of each step's reads and
+// MFMAs to the compiler.  Measured: one step ahead is faster with one scale
+// per row (per-channel), while with group-wise scales, whose per-block scale
+// and zero-point registers already hold the kernel at its register limit,
+// the compiler's order is.
+#ifndef SPEAR_WIDE_LOOKAHEAD128_PC
+#define SPEAR_WIDE_LOOKAHEAD128_PC 1
+#endif
+#ifndef SPEAR_WIDE_LOOKAHEAD128
+#define SPEAR_WIDE_LOOKAHEAD128 0
+#endif
 #ifndef SPEAR_WIDE_FORCE_KSP
 #define SPEAR_WIDE_FORCE_KSP 0  // > 0: that many K-splits (or the nearest count with no empty split)
 #endif
@@ -186,15 +200,21 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   }
 
   // Groups of D blocks.  Group g's activation columns (kx0 + g D 128 ..) for
-  // every token are one staged chunk: loaded into registers (2 MB pieces of
-  // 16 bytes per thread) during group g - 1, stored to LDS between two
-  // barriers at the start of group g.  Every address is clamped into its
+  // every token are one staged chunk, loaded into registers (2 MB pieces of
+  // 16 bytes per thread) a group ahead.  Every address is clamped into its
   // array and every load is issued unconditionally, so a group is
   // straight-line code whose waits count its loads exactly; columns past the
   // split's end or past K are staged as zeros, which makes the padding blocks
   // of the last group add exact zeros.
+  //  * Up to 64 tokens (kDB) the chunks alternate between two LDS buffers:
+  //    chunk g + 1 is stored at the end of group g, then one barrier, after
+  //    which every wave has finished reading chunk g's buffer (which chunk
+  //    g + 2 overwrites) and chunk g + 1 is complete.
+  //  * At 128 tokens one buffer: stored at the start of group g, between two
+  //    barriers.
   constexpr int kPieces = 2 * MB;  // (16 MB tokens x D 128 / 8 pieces) / 512 threads, D = 4
   static_assert(D == 4, "one staged chunk per group of four blocks");
+  constexpr bool kDB = MB <= 4;
   u32x4_t xr[kPieces];
   auto xload = [&](int g) {
 #pragma unroll
@@ -205,11 +225,13 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
       xr[i] = *(const u32x4_t *)(a.x + (size_t)m * a.K + k);
     }
   };
+  auto xbuf = [&](int g) { return kDB ? lds + (g & 1) * a.buf_halves : lds; };
   // Only the split's last group reaches past its end (or past K): its
   // columns there are staged as zeros, through a bit mask.  Rows past M hold
   // copies of row M - 1 (xload clamps), which no kept output reads.
   auto xstore = [&](int g, auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
+    uint16_t *dst = xbuf(g);
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
       const int p = tid + kThreads * i;
@@ -219,7 +241,7 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
         const uint32_t keep = (kx0 + g * kChunkCols + 8 * j < kend) ? ~0u : 0u;
         v = u32x4_t{v[0] & keep, v[1] & keep, v[2] & keep, v[3] & keep};
       }
-      *(u32x4_t *)(lds + m * kXStr + 8 * xplace(j)) = permute_8(v);
+      *(u32x4_t *)(dst + m * kXStr + 8 * xplace(j)) = permute_8(v);
     }
   };
 
@@ -242,8 +264,8 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   };
 
   // the same order of loads as each group issues them (activation chunk,
-  // then the ring), so that the waits at the top of the loop count the same
-  // loads whether the loop is entered or repeated
+  // then the ring), so that the waits in the loop count the same loads
+  // whether the loop is entered or repeated
   xload(0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -263,19 +285,28 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) xrow[mb] = min(col + 16 * mb, a.M - 1) * kXStr;
 
-  // Each ring slot is dequantized before its refill is issued, so the refill
-  // can load into the slot's own registers: a slot still live when its
-  // refill issues would take a register copy at the loop's back edge, and
-  // that copy waits for the load, draining the ring every group.
-  const int ngr = (nbl + D - 1) / D;
-  auto run_group = [&](int g, auto mask_tag) {
-    lds_barrier();  // every wave is done with group g - 1's chunk
-    xstore(g, mask_tag);
-    lds_barrier();
-    xload(g + 1);     // clamped: past the split it reloads valid columns, staged as zeros
-    // keep the prefetches here: the scheduler would otherwise move loads whose
-    // results are only used by the next group down to just before that use
-    __builtin_amdgcn_sched_barrier(0);
+  // One group's blocks.  Each ring slot is dequantized before its refill is
+  // issued, so the refill can load into the slot's own registers: a slot
+  // still live when its refill issues would take a register copy at the
+  // loop's back edge, and that copy waits for the load, draining the ring
+  // every group.  The x fragments of the group's 4 D steps (block i, step t)
+  // are read kLookahead steps ahead of their MFMAs, the order pinned by
+  // scheduling barriers, so that the LDS latency overlaps the MFMAs of the
+  // steps before (with kLookahead 0, each step reads its own, in an order
+  // the compiler chooses).
+  constexpr int kSteps = 4 * D;
+  constexpr int kLookahead = MB <= 4 ? SPEAR_WIDE_LOOKAHEAD
+                                     : (PERCH ? SPEAR_WIDE_LOOKAHEAD128_PC : SPEAR_WIDE_LOOKAHEAD128);
+  auto blocks = [&](int g) {
+    const uint16_t *xg = xbuf(g) + 8 * xplace(4 * h);
+    u32x4_t xq[kSteps][MB];
+    auto xread = [&](int st) {
+      const uint16_t *xb = xg + 8 * xplace(16 * (st >> 2)) + 8 * (st & 3);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) xq[st][mb] = *(const u32x4_t *)(xb + xrow[mb]);
+    };
+#pragma unroll
+    for (int st = 0; st < kLookahead; ++st) xread(st);
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       const int b = g * D + i;
@@ -296,25 +327,29 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
 #pragma unroll
       for (int r = 0; r < R; ++r) wload(b + D, r, ring[i][r], sr[i][r], zr[i][r]);
       __builtin_amdgcn_sched_barrier(0);
-      const uint16_t *xb = lds + 8 * (xplace(16 * i) + xplace(4 * h));
       f32x4_t gacc[R][MB];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        u32x4_t xa[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) xa[mb] = *(const u32x4_t *)(xb + xrow[mb] + 8 * t);
+        const int st = 4 * i + t;
+        if constexpr (kLookahead == 0) {
+          xread(st);
+        } else {
+          if (st + kLookahead < kSteps) xread(st + kLookahead);
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             if constexpr (PERCH) {
-              acc[r][mb] = mfma_16x16x32<DT>(xa[mb], bop[r][t], acc[r][mb]);
+              acc[r][mb] = mfma_16x16x32<DT>(xq[st][mb], bop[r][t], acc[r][mb]);
             } else {
-              gacc[r][mb] = mfma_16x16x32<DT>(xa[mb], bop[r][t],
+              gacc[r][mb] = mfma_16x16x32<DT>(xq[st][mb], bop[r][t],
                                               t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : gacc[r][mb]);
             }
           }
         }
+        if constexpr (kLookahead > 0) __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (!PERCH) {
 #pragma unroll
@@ -324,9 +359,47 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
       }
     }
   };
-  // every group but the last as one loop of straight-line code, then the last
-  for (int g = 0; g + 1 < ngr; ++g) run_group(g, std::false_type{});
-  run_group(ngr - 1, std::true_type{});
+
+  const int ngr = (nbl + D - 1) / D;
+  if constexpr (kDB) {
+    if (ngr == 1)
+      xstore(0, std::true_type{});
+    else
+      xstore(0, std::false_type{});
+    xload(1);  // clamped: past the split it reloads valid columns, never stored
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    // every group but the last two, then the one that stores the last
+    // (masked) chunk, then the last
+    for (int g = 0; g + 2 < ngr; ++g) {
+      blocks(g);
+      xstore(g + 1, std::false_type{});
+      xload(g + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+    }
+    if (ngr >= 2) {
+      blocks(ngr - 2);
+      xstore(ngr - 1, std::true_type{});
+      lds_barrier();
+    }
+    blocks(ngr - 1);
+  } else {
+    auto run_group = [&](int g, auto mask_tag) {
+      lds_barrier();  // every wave is done with group g - 1's chunk
+      xstore(g, mask_tag);
+      lds_barrier();
+      xload(g + 1);  // clamped: past the split it reloads valid columns, staged as zeros
+      // keep the prefetches here: the scheduler would otherwise move loads
+      // whose results are only used by the next group down to just before
+      // that use
+      __builtin_amdgcn_sched_barrier(0);
+      blocks(g);
+    };
+    // every group but the last as one loop of straight-line code, then the last
+    for (int g = 0; g + 1 < ngr; ++g) run_group(g, std::false_type{});
+    run_group(ngr - 1, std::true_type{});
+  }
   if constexpr (PERCH) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -354,15 +427,11 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   }
 }
 
-// Workgroups per CU: two for the 64-token kernel with one row block per wave
-// (its registers and its 66 KB of staged x allow it), else one.
-template <int MB, int R>
-constexpr int wgs_per_cu() {
-  return (MB == 4 && R == 1) ? 2 : 1;
-}
-
+// One workgroup per CU: its 8 waves are 2 per SIMD (the launch bound's
+// second figure, waves per SIMD, lets each use up to 256 registers), and the
+// staged x takes most of the LDS.
 template <int DT, int MB, int R, int D, bool EC, bool PERCH>
-__global__ __launch_bounds__(kThreads, (wgs_per_cu<MB, R>())) void wide_kernel(WideArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void wide_kernel(WideArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, b = blockIdx.x;
   if constexpr (EC) {
@@ -439,7 +508,7 @@ WidePlan plan_wide(const LayerDesc &L, int M) {
   p.nb = (L.K + 127) / 128;
   const int tile_rows = 16 * p.r * kWaves;
   p.n_tiles = (L.N + tile_rows - 1) / tile_rows;
-  const int resident = 256 * ((p.mb == 4 && p.r == 1) ? 2 : 1);
+  const int resident = 256;  // one workgroup per CU
   const double wbytes = (double)L.N * L.K / 2;
   double best = 1e30;
   for (int ks = 1; ks <= std::min(SPEAR_WIDE_MAX_KSP, p.nb); ++ks) {
@@ -461,7 +530,8 @@ WidePlan plan_wide(const LayerDesc &L, int M) {
   }
   p.direct = L.rank == 0 && p.ksp == 1;
   p.buf_halves = 16 * p.mb * kXStr;
-  p.red_off = (int)round256((size_t)p.buf_halves * 2);
+  // up to 64 tokens the staged chunks alternate between two buffers
+  p.red_off = (int)round256((size_t)p.buf_halves * 2 * (p.mb <= 4 ? 2 : 1));
   p.lds = p.red_off + (size_t)kWaves * 64 * 16;  // the producers' wave sums
   p.tp_off = kWsDataOff;
   p.u_off = p.tp_off + (L.rank > 0 ? round256((size_t)p.ks * M * p.rp1 * sizeof(float)) : 0);
