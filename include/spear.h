@@ -186,8 +186,12 @@ spear_status_t spear_tile_int4(const int32_t *words, int32_t *qweight, int64_t N
  * Decode path (2.2 A, decode phase): one fused kernel launch for 1 <= M <= 128
  * tokens.  Up to 32 tokens, workgroups own groups of 16 to 128 output rows
  * over all of K (or K-splits, see below); from 33 tokens on, workgroups own
- * tiles of 256 output rows over a K-split each and stream x through LDS, so
- * that each staged activation fragment feeds many rows.
+ * tiles of 128 output rows over a K-split each and stream x through LDS, so
+ * that each staged activation fragment feeds many rows, and the last split to
+ * finish a tile sums its partials in split order and adds the compensator.
+ * (From 33 tokens, with the per-rank gate, or with K-splits over more than
+ * 128 tiles, two more launches on the same stream do that: one forms the
+ * compensator's gated sums, a finish kernel adds them and the partials.)
  * x [M][K] and y [M][N] are row-major activation-type device arrays, x and y
  * 16-byte aligned.  The gate, A x and the gated B (A x) term are computed in
  * the same launch as the 4-bit product and added before y is rounded.

@@ -87,6 +87,31 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Four consecutive fp32 values published by another workgroup, read
+// coherently across the XCDs' L2 caches (cache policy sc1, as a relaxed
+// agent-scope atomic load has).
+__device__ __forceinline__ f32x4_t load_partials4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return bitcast<f32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16));
+}
+
+// The same four values stored for other workgroups (sc1: written through to
+// the level every XCD reads with sc1 loads).
+__device__ __forceinline__ void store_partials4(f32x4_t v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(bitcast<u32x4_t>(v), r, byte_off, 0, 16);
+}
+
+// Completion of this wave's agent-scope stores before the count that
+// publishes them.  Those stores (sc1) are written through to the level that
+// every XCD reads with sc1 loads, so they need no write-back of the L2, only
+// an s_waitcnt vmcnt(0) (gfx9 counts stores in vmcnt; this encoding leaves
+// expcnt and lgkmcnt at their maxima).  The signal fences keep the compiler
+// from moving memory operations across the wait.
+__device__ __forceinline__ void publish_wait() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Per-row zero-point constant for dequant_word.
 //   fp16: packed pair of -(1024 + z) (exact: 1024 + z is an integer < 2048).
 //   bf16: 2^23 + z as an fp32 bit pattern.

@@ -87,6 +87,7 @@ struct WidePlan {
   int nb, n_tiles, ksp, nbs;
   int buf_halves, red_off;
   bool direct;           // rank 0, one split: the main kernel writes y itself
+  bool fused;            // one launch: the kernel finishes its tiles (split sums, U B^T)
   size_t lds;
   size_t tp_off, u_off, part_off, end;  // workspace: [A; w_g] x sums, U, partial outputs
 };
@@ -95,7 +96,6 @@ size_t wide_workspace_bytes(const LayerDesc &L, int M);
 void describe_wide(const LayerDesc &L, int M, spear_plan_t *out);
 hipError_t launch_wide(const LayerDesc &L, int dtype, const uint16_t *x, uint16_t *y, int M,
                        void *ws, hipStream_t s);
-int wide_launches(const LayerDesc &L, int M);  // kernel launches of one wide call
 
 // Decode, dispatched per call to one of two compilations of the same kernels
 // (8 or 4 waves per workgroup; decode.hip picks).

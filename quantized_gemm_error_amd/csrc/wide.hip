@@ -58,6 +58,7 @@ __host__ __device__ constexpr int xplace(int p) {
   return (p & 0x2B) | ((p >> 2) & 1) << 4 | ((p >> 4) & 1) << 2;
 }
 constexpr int kMaxLds = 160 * 1024;
+constexpr int kMaxProducerSplits = 8;  // wide_producer_ksplit's largest count
 // Launch-shape constants of plan_wide (measured on MI355X).
 #ifndef SPEAR_WIDE_R64
 #define SPEAR_WIDE_R64 1  // 16-row blocks per wave at up to 64 tokens
@@ -99,7 +100,85 @@ struct WideArgs {
   float *part;      // partial outputs [ksp][M][N] (null: y directly)
   int buf_halves;   // halves of the staged x chunk (16 MB rows x kXStr)
   int red_off;      // byte offset of the producers' wave sums in dynamic LDS
+  // one launch for the whole call (fused): the kernel finishes its tiles
+  int fused;
+  WsHeader *hdr;          // counters: producers (arrive), K-splits per tile, counting out
+  float *U;               // [M][rp1]: U = g (A x), formed by the last producer
+  const uint16_t *B;      // [N][rank]
+  float b_gate;
+  uint32_t spin_limit;    // polls of the producers' count before computing U itself
+  int part_bytes;         // bytes of the partial-tile pieces (fused, ksp > 1)
 };
+
+// Fused launch: workgroup b counts itself out in slot b % 8 once it reads the
+// producers' count no more; the one that completes every slot resets the
+// counters (the scheme of the decode launch), so the workspace is left at
+// zero for the next call.  tile_piece_off is the byte offset of the 16-byte
+// piece (lane) of a partial tile: split q, tile t, wave w, row block r,
+// token block mb.
+constexpr uint32_t kNotCounted = 0xFFFFFFFFu;
+__device__ __forceinline__ uint32_t count_out(const WideArgs &a) {
+  return __hip_atomic_fetch_add(&a.hdr->done[blockIdx.x % 8].v, 1u, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ void finish_after(const WideArgs &a, uint32_t old) {
+  const uint32_t g = gridDim.x, slot = blockIdx.x % 8;
+  const uint32_t in_slot = (g - 1 - slot) / 8 + 1;
+  if (old + 1 != in_slot) return;
+  const uint32_t slots = g < 8 ? g : 8;
+  const uint32_t top = __hip_atomic_fetch_add(&a.hdr->done_top.v, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  if (top + 1 != slots) return;
+  __hip_atomic_store(&a.hdr->arrive.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&a.hdr->done_top.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < 8; ++i)
+    __hip_atomic_store(&a.hdr->done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <int R, int MB>
+__device__ __forceinline__ int tile_piece_off(const WideArgs &a, int q, int t, int w, int r, int mb,
+                                              int lane) {
+  return (((((q * a.n_tiles + t) * kWaves + w) * R + r) * MB + mb) * 64 + lane) * 16;
+}
+
+// U = g (A x) from the producers' K-split sums, by the last producer of a
+// fused launch: for token m, t_j = sum_q tp[q][m][j] (j < rank) and z = the
+// same sum of row rank, each in split order; g = sigmoid(z + b_g); U[m][j] =
+// g t_j, zeros in columns rank .. rp1 - 1 (as prefill_u_kernel forms it).
+// The sums are read and U is stored with sc1 (every producer published its
+// sums before counting itself in).
+__device__ void form_u(const WideArgs &a, int tid) {
+  const size_t stride = (size_t)a.M * a.rp1;
+  const int q4 = a.rp1 / 4;
+  const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
+      a.tp, (short)0, (int)(a.ks * stride * sizeof(float)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
+      a.U, (short)0, (int)(stride * sizeof(float)), 0x00020000);
+  for (int i = tid; i < a.M * q4; i += kThreads) {
+    const int m = i / q4, j = 4 * (i - m * q4);
+    f32x4_t v[kMaxProducerSplits];
+    float w[kMaxProducerSplits];
+#pragma unroll
+    for (int q = 0; q < kMaxProducerSplits; ++q) {
+      const int qq = min(q, a.ks - 1);
+      const int base = (int)((qq * stride + (size_t)m * a.rp1) * sizeof(float));
+      v[q] = load_partials4(tr, base + j * 4);
+      w[q] = bitcast<float>(__builtin_amdgcn_raw_buffer_load_b32(tr, base + a.rank * 4, 0, 16));
+    }
+    f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+    float z = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMaxProducerSplits; ++q)
+      if (q < a.ks) {
+        t += v[q];
+        z += w[q];
+      }
+    const float g = gate_sigmoid(z + a.b_gate);
+    f32x4_t u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) u[c] = (j + c < a.rank) ? g * t[c] : 0.f;
+    store_partials4(u, ur, (m * a.rp1 + j) * 4);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Producers: one 16-row block of [A; w_g] over one K-split, for every token;
@@ -157,17 +236,230 @@ __device__ void produce(const WideArgs &a, int p, f32x4_t *red, int tid) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 16 * mb + 4 * h + e;
-        if (jin && m < a.M) dst[(size_t)m * a.rp1] = v[e];
+        if (jin && m < a.M) {
+          if (a.fused)  // read by the last producer of this launch: written through (sc1)
+            __hip_atomic_store((uint32_t *)&dst[(size_t)m * a.rp1], bitcast<uint32_t>(v[e]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            dst[(size_t)m * a.rp1] = v[e];
+        }
       }
     }
     __syncthreads();
+  }
+  if (!a.fused) return;
+  // Fused launch: count in.  The producer that completes the count forms U
+  // and counts in once more, so the consumers' wait is for producers + 1.
+  // The stores complete before each count (publish_wait), and each count is
+  // performed before this workgroup counts itself out.
+  volatile int *last = (volatile int *)red;
+  if (wave == 0) publish_wait();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&a.hdr->arrive.v, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    *last = (old + 1 == (uint32_t)a.producers) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*last) {
+    form_u(a, tid);
+    publish_wait();
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_fetch_add(&a.hdr->arrive.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid == 0) {
+    publish_wait();
+    finish_after(a, count_out(a));
+  }
+}
+
+// U without the producers (their count was not seen within the wait): the
+// sums t = [A; w_g] x of every token straight from global memory in fp32
+// (column rank holds the gate's z), then U = g t in place.  Ends with a
+// barrier.
+template <int DT>
+__device__ void self_u(const WideArgs &a, float *ul, int tid) {
+  for (int e = tid; e < a.M * a.rows; e += kThreads) {
+    const int m = e / a.rows, j = e - m * a.rows;
+    const uint16_t *arow = j < a.rank ? a.A + (size_t)j * a.K : a.wg;
+    const uint16_t *xrow = a.x + (size_t)m * a.K;
+    float t = 0.f;
+    for (int k = 0; k < a.K; k += 8) {
+      const u16x8_t av = *(const u16x8_t *)(arow + k);
+      const u16x8_t xv = *(const u16x8_t *)(xrow + k);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) t += to_f32<DT>(av[c]) * to_f32<DT>(xv[c]);
+    }
+    ul[m * a.rp1 + j] = t;
+  }
+  __syncthreads();
+  for (int e = tid; e < a.M * a.rank; e += kThreads) {
+    const int m = e / a.rank, j = e - m * a.rank;
+    ul[m * a.rp1 + j] *= gate_sigmoid(ul[m * a.rp1 + a.rank] + a.b_gate);
+  }
+  __syncthreads();
+}
+
+// The end of a fused launch's consumer: this split's fp32 tile (acc, scale
+// applied) becomes y.
+//  * K-splits (ksp > 1): each split publishes its tile (sc1 stores, then
+//    their completion) and counts itself in on the tile's counter; the split
+//    that completes the count sums the ksp tiles in split order, its own from
+//    registers, and resets the counter.  The others are done.
+//  * Compensator: after a bounded wait for the producers' count plus the
+//    last producer's U (on expiry the workgroup computes U itself and sets
+//    bit 0 of the workspace flags), U goes to LDS and each wave adds U B^T
+//    with fp32 16x16x4 MFMAs, rank steps in order.
+// y is rounded once.  This is the arithmetic, in the same order, of the
+// finish kernel that completes the three-launch form.
+template <int DT, int MB, int R, bool EC>
+__device__ void finish_tile(const WideArgs &a, const f32x4_t (&acc)[R][MB], int q, int tile,
+                            const int (&row)[R], uint16_t *lds, int tid) {
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 15, h = lane >> 4;
+  const int n0 = tile * 16 * R * kWaves;
+  volatile int *vote = (volatile int *)((char *)lds + a.red_off);
+  uint32_t counted = kNotCounted;
+  f32x4_t v[R][MB];
+  if (a.ksp > 1) {
+    const __amdgpu_buffer_rsrc_t pr =
+        __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        store_partials4(acc[r][mb], pr, tile_piece_off<R, MB>(a, q, tile, wave, r, mb, lane));
+    publish_wait();
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(&a.hdr->tile[tile].v, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      vote[0] = (old + 1 == (uint32_t)a.ksp) ? 1 : 0;
+    }
+    __syncthreads();
+    if (vote[0] == 0) {  // uniform: another split completes this tile
+      if (EC && tid == 0) finish_after(a, count_out(a));
+      return;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) v[r][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int kQB = MB <= 4 ? 4 : 2;  // splits whose pieces are in flight together
+    for (int q0 = 0; q0 < a.ksp; q0 += kQB) {
+      f32x4_t pv[kQB][R][MB];
+#pragma unroll
+      for (int i = 0; i < kQB; ++i)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            pv[i][r][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // the other splits only: uncached loads are costly per CU
+            if (q0 + i < a.ksp && q0 + i != q)
+              pv[i][r][mb] =
+                  load_partials4(pr, tile_piece_off<R, MB>(a, q0 + i, tile, wave, r, mb, lane));
+          }
+#pragma unroll
+      for (int i = 0; i < kQB; ++i)
+        if (q0 + i < a.ksp) {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) v[r][mb] += (q0 + i == q) ? acc[r][mb] : pv[i][r][mb];
+        }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) v[r][mb] = acc[r][mb];
+  }
+
+  if constexpr (EC) {
+    const int nst = (a.rank + 3) / 4;
+    // B for the first eight rank steps does not depend on the producers
+    float bv[R][8];
+    auto bload = [&](int st0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = min(4 * min(st0 + i, nst - 1) + h, a.rank - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) bv[r][i] = to_f32<DT>(a.B[(size_t)row[r] * a.rank + j]);
+      }
+    };
+    bload(0);
+    __syncthreads();  // every wave is done with the staged x (the LDS takes U next)
+    if (tid == 0) {
+      int expired = 0;
+      for (uint32_t it = 0;; ++it) {
+        if (it >= a.spin_limit) {
+          expired = 1;
+          __hip_atomic_fetch_or(&a.hdr->flags.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        if (__hip_atomic_load(&a.hdr->arrive.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+            (uint32_t)a.producers + 1u)
+          break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      vote[1] = expired;
+    }
+    __syncthreads();
+    if (tid == 0) counted = count_out(a);  // the count is read no more
+    float *ul = (float *)lds;  // U [M][rp1]
+    if (vote[1] == 0) {
+      const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
+          a.U, (short)0, a.M * a.rp1 * (int)sizeof(float), 0x00020000);
+      for (int i = tid; i < a.M * (a.rp1 / 4); i += kThreads)
+        *(f32x4_t *)(ul + 4 * i) = load_partials4(ur, 16 * i);
+      __syncthreads();
+    } else {
+      self_u<DT>(a, ul, tid);
+    }
+    for (int st0 = 0; st0 < nst; st0 += 8) {
+      if (st0 > 0) bload(st0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = 4 * (st0 + i) + h;
+        if (st0 + i < nst) {
+          const bool jin = j < a.rank;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const int m = col + 16 * mb;
+            const float u = (jin && m < a.M) ? ul[m * a.rp1 + j] : 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) v[r][mb] = mfma_16x16x4_f32(u, jin ? bv[r][i] : 0.f, v[r][mb]);
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = n0 + 16 * (wave * R + r) + col;
+    if (n < a.N) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 16 * mb + 4 * h + e;
+          if (m < a.M) a.y[(size_t)m * a.N + n] = from_f32<DT>(v[r][mb][e]);
+        }
+    }
+  }
+  if (tid == 0) {
+    if (a.ksp > 1)
+      __hip_atomic_store(&a.hdr->tile[tile].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (EC) finish_after(a, counted);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Consumers.
 // ---------------------------------------------------------------------------
-template <int DT, int MB, int R, int D, bool PERCH>
+template <int DT, int MB, int R, int D, bool EC, bool PERCH, bool FUSED>
 __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, col = lane & 15, h = lane >> 4;
@@ -407,30 +699,36 @@ __device__ void consume(const WideArgs &a, int c, uint16_t *lds, int tid) {
       for (int mb = 0; mb < MB; ++mb) acc[r][mb] *= s_row[r];
   }
 
+  if constexpr (!FUSED) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int n = n0 + 16 * (wave * R + r) + col;
-    if (n < a.N) {
+    for (int r = 0; r < R; ++r) {
+      const int n = n0 + 16 * (wave * R + r) + col;
+      if (n < a.N) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = 16 * mb + 4 * h + e;
-          if (m < a.M) {
-            if (a.part)
-              a.part[((size_t)q * a.M + m) * a.N + n] = acc[r][mb][e];
-            else
-              a.y[(size_t)m * a.N + n] = from_f32<DT>(acc[r][mb][e]);
+          for (int e = 0; e < 4; ++e) {
+            const int m = 16 * mb + 4 * h + e;
+            if (m < a.M) {
+              if (a.part)
+                a.part[((size_t)q * a.M + m) * a.N + n] = acc[r][mb][e];
+              else
+                a.y[(size_t)m * a.N + n] = from_f32<DT>(acc[r][mb][e]);
+            }
           }
-        }
+      }
     }
+  } else {
+    finish_tile<DT, MB, R, EC>(a, acc, q, tile, row, lds, tid);
   }
 }
 
 // One workgroup per CU: its 8 waves are 2 per SIMD (the launch bound's
 // second figure, waves per SIMD, lets each use up to 256 registers), and the
-// staged x takes most of the LDS.
-template <int DT, int MB, int R, int D, bool EC, bool PERCH>
+// staged x takes most of the LDS.  FUSED: the one-launch form (the tile
+// finishing is compiled only into it, so the other form keeps its
+// registers for the main loop).
+template <int DT, int MB, int R, int D, bool EC, bool PERCH, bool FUSED>
 __global__ __launch_bounds__(kThreads, 2) void wide_kernel(WideArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, b = blockIdx.x;
@@ -439,15 +737,15 @@ __global__ __launch_bounds__(kThreads, 2) void wide_kernel(WideArgs a) {
       produce<DT, MB>(a, b, (f32x4_t *)((char *)lds + a.red_off), tid);
       return;
     }
-    consume<DT, MB, R, D, PERCH>(a, b - a.producers, lds, tid);
+    consume<DT, MB, R, D, true, PERCH, FUSED>(a, b - a.producers, lds, tid);
   } else {
-    consume<DT, MB, R, D, PERCH>(a, b, lds, tid);
+    consume<DT, MB, R, D, false, PERCH, FUSED>(a, b, lds, tid);
   }
 }
 
-template <int DT, int MB, int R, bool EC, bool PERCH>
+template <int DT, int MB, int R, bool EC, bool PERCH, bool FUSED>
 hipError_t launch_t(const WideArgs &a, int grid, size_t lds, hipStream_t s) {
-  auto kern = wide_kernel<DT, MB, R, kCb, EC, PERCH>;
+  auto kern = wide_kernel<DT, MB, R, kCb, EC, PERCH, FUSED>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -459,22 +757,30 @@ hipError_t launch_t(const WideArgs &a, int grid, size_t lds, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT, int MB, int R>
+template <int DT, int MB, int R, bool FUSED>
 hipError_t launch_ec(const WideArgs &a, int grid, size_t lds, bool ec, bool perch, hipStream_t s) {
-  if (ec) return perch ? launch_t<DT, MB, R, true, true>(a, grid, lds, s)
-                       : launch_t<DT, MB, R, true, false>(a, grid, lds, s);
-  return perch ? launch_t<DT, MB, R, false, true>(a, grid, lds, s)
-               : launch_t<DT, MB, R, false, false>(a, grid, lds, s);
+  if (ec) return perch ? launch_t<DT, MB, R, true, true, FUSED>(a, grid, lds, s)
+                       : launch_t<DT, MB, R, true, false, FUSED>(a, grid, lds, s);
+  return perch ? launch_t<DT, MB, R, false, true, FUSED>(a, grid, lds, s)
+               : launch_t<DT, MB, R, false, false, FUSED>(a, grid, lds, s);
+}
+
+template <int DT, int MB, int R>
+hipError_t launch_fused(const WideArgs &a, int grid, size_t lds, bool ec, bool perch, bool fused,
+                        hipStream_t s) {
+  return fused ? launch_ec<DT, MB, R, true>(a, grid, lds, ec, perch, s)
+               : launch_ec<DT, MB, R, false>(a, grid, lds, ec, perch, s);
 }
 
 template <int DT>
 hipError_t launch_mb(const WideArgs &a, const WidePlan &p, bool ec, bool perch, hipStream_t s) {
   const int grid = p.n_tiles * p.ksp + p.producers;
   if (p.mb == 4) {
-    return p.r == 1 ? launch_ec<DT, 4, 1>(a, grid, p.lds, ec, perch, s)
-                    : launch_ec<DT, 4, 2>(a, grid, p.lds, ec, perch, s);
+    return p.r == 1 ? launch_fused<DT, 4, 1>(a, grid, p.lds, ec, perch, p.fused, s)
+                    : launch_fused<DT, 4, 2>(a, grid, p.lds, ec, perch, p.fused, s);
   }
-  return launch_ec<DT, 8, 1>(a, grid, p.lds, ec, perch, s);  // 128 tokens: one row block per wave
+  // 128 tokens: one row block per wave
+  return launch_fused<DT, 8, 1>(a, grid, p.lds, ec, perch, p.fused, s);
 }
 
 // K-splits of the producers: about 2048 columns each, from 4 to 8.
@@ -517,7 +823,8 @@ WidePlan plan_wide(const LayerDesc &L, int M) {
     if (ksp != ks) continue;
     const int wgs = p.n_tiles * ksp;
     const double live = std::min(wgs, resident);
-    const bool parts = ksp > 1 || L.rank > 0;
+    // fp32 partial outputs: with K-splits, or for the per-rank gate's finish kernel
+    const bool parts = ksp > 1 || L.rg_hidden > 0;
     const double part = parts ? (double)ksp * L.N * M * 4 : 0.0;
     double t = std::max(wbytes / (live * SPEAR_WIDE_WG_RATE), (wbytes + part) / 5e12) +
                part / 8e12;
@@ -529,6 +836,15 @@ WidePlan plan_wide(const LayerDesc &L, int M) {
     }
   }
   p.direct = L.rank == 0 && p.ksp == 1;
+  // One launch finishes the tiles (the K-splits' sums through the tile
+  // counters, the scalar gate's U from the last producer); the per-rank gate
+  // keeps its U kernel and the finish kernel, as do K-split calls with more
+  // tiles than the header has counters.  Measured: at 128 tokens with the
+  // compensator and three or more K-splits the two extra launches are
+  // faster (the tile's one finishing workgroup then adds U B^T for 128 tokens
+  // after its main loop, where the finish kernel spreads that work).
+  p.fused = !p.direct && L.rg_hidden == 0 && (p.ksp == 1 || p.n_tiles <= kMaxSplitTiles) &&
+            !(L.rank > 0 && p.mb == 8 && p.ksp >= 3);
   p.buf_halves = 16 * p.mb * kXStr;
   // up to 64 tokens the staged chunks alternate between two buffers
   p.red_off = (int)round256((size_t)p.buf_halves * 2 * (p.mb <= 4 ? 2 : 1));
@@ -536,7 +852,12 @@ WidePlan plan_wide(const LayerDesc &L, int M) {
   p.tp_off = kWsDataOff;
   p.u_off = p.tp_off + (L.rank > 0 ? round256((size_t)p.ks * M * p.rp1 * sizeof(float)) : 0);
   p.part_off = p.u_off + (L.rank > 0 ? round256((size_t)M * p.rp1 * sizeof(float)) : 0);
-  p.end = p.direct ? 0 : p.part_off + round256((size_t)p.ksp * M * L.N * sizeof(float));
+  // partial outputs: fused, the K-splits' tiles as 16-byte pieces of each
+  // wave's fragments (tile_piece_off); else [ksp][M][N] for the finish kernel
+  const size_t part_bytes =
+      p.fused ? (p.ksp > 1 ? (size_t)p.ksp * p.n_tiles * tile_rows * 16 * p.mb * sizeof(float) : 0)
+              : (size_t)p.ksp * M * L.N * sizeof(float);
+  p.end = p.direct ? 0 : p.part_off + round256(part_bytes);
   p.ok = p.lds <= (size_t)kMaxLds;
   return p;
 }
@@ -544,11 +865,6 @@ WidePlan plan_wide(const LayerDesc &L, int M) {
 size_t wide_workspace_bytes(const LayerDesc &L, int M) {
   const WidePlan p = plan_wide(L, M);
   return p.ok ? p.end : 0;
-}
-
-int wide_launches(const LayerDesc &L, int M) {
-  const WidePlan p = plan_wide(L, M);
-  return p.direct ? 1 : (L.rank > 0 ? 3 : 2);
 }
 
 void describe_wide(const LayerDesc &L, int M, spear_plan_t *out) {
@@ -592,10 +908,17 @@ hipError_t launch_wide(const LayerDesc &L, int dtype, const uint16_t *x, uint16_
   a.part = p.direct ? nullptr : (float *)(base + p.part_off);
   a.buf_halves = p.buf_halves;
   a.red_off = p.red_off;
+  a.fused = p.fused ? 1 : 0;
+  a.hdr = (WsHeader *)ws;
+  a.U = L.rank > 0 ? (float *)(base + p.u_off) : nullptr;
+  a.B = L.B;
+  a.b_gate = L.b_gate;
+  a.spin_limit = get_decode_spin_limit();
+  a.part_bytes = (int)(p.end - p.part_off);
   const bool ec = L.rank > 0;
   hipError_t e = dtype == DT_F16 ? launch_mb<DT_F16>(a, p, ec, L.per_channel, s)
                                  : launch_mb<DT_BF16>(a, p, ec, L.per_channel, s);
-  if (e != hipSuccess || p.direct) return e;
+  if (e != hipSuccess || p.direct || p.fused) return e;
   float *U = nullptr;
   if (ec) {
     U = (float *)(base + p.u_off);

@@ -231,6 +231,7 @@ WIDE_CASES = [
     (96, 512, 128, 40, 64, "f16", True, 64),      # per-rank gate, widest hidden layer
     (300, 2048, 0, 24, 90, "bf16", True, 8),      # per-rank gate, 128-token kernel
     (33000, 256, 128, 16, 40, "f16", False, 0),   # 129 tiles: more than the tile counters, no K split
+    (16512, 4096, 128, 16, 64, "f16", False, 0),  # 129 tiles with K-splits: the three-launch form
 ]
 
 
@@ -255,20 +256,34 @@ def test_decode_wide_parity(N, K, G, r, M, dtype, outl, hidden):
     assert _ws_header(ws) == [0] * 12
 
 
-@pytest.mark.parametrize("M", [48, 100])
-def test_decode_wide_never_waits(M):
-    """The wide launch has no wait between workgroups (its compensator and split sums are
-    joined by kernel boundaries): with the poll limit at 0 it still matches the oracle and
-    sets no flag."""
-    note(f"decode wide, poll limit 0, M={M}")
-    hl, xb, lay, x = _setup(700, 2048, 128, 32, seed=M + 3, M=M, outliers=True, b_gate=0.3)
+@pytest.mark.parametrize("N,K,M,hidden,one_launch", [
+    (700, 2048, 48, 0, True),     # 8 K-splits, 64-token kernel
+    (3000, 512, 100, 0, True),    # 2 K-splits, 128-token kernel
+    (8192, 512, 100, 0, True),    # no K-split: every workgroup finishes its tile
+    (700, 2048, 100, 0, False),   # 8 K-splits at 128 tokens: U and finish launches
+    (700, 2048, 48, 8, False),    # per-rank gate: U and finish launches
+])
+def test_decode_wide_wait_expiry(N, K, M, hidden, one_launch):
+    """With no wait at all for the producers (poll limit 0, set on the host), the one-launch
+    wide form computes U itself in every workgroup that finishes a tile: the output still
+    matches the oracle, bit 0 of the workspace flags records the expiry and the counters are
+    back at zero.  The three-launch form (per-rank gate; the compensator at 128 tokens with
+    three or more K-splits) has no wait and sets no flag.  Every kernel exits normally."""
+    note(f"decode wide, poll limit 0, N={N} K={K} M={M} hidden={hidden}")
+    hl, xb, lay, x = _setup(N, K, 128, 32, seed=M + 3, M=M, outliers=True, b_gate=0.3)
+    params = None
+    if hidden:
+        params = synth.make_rank_gate(32, hidden, seed=M, t_scale=0.01 * np.sqrt(K))
+        lay.rank_gate = spear.rank_gate_to_device(params, 0.9, DEV)
     with decode_spin_limit(0):
         ws = spear.new_workspace(lay, M)
         y = spear.spear_linear_decode(lay, x, workspace=ws)
         torch.cuda.synchronize()
-    assert_close(gpu_y_f64(y, "f16"), oracle_y(hl, xb), "wide, poll limit 0")
-    assert spear.spear_workspace_flags(ws) == 0
-    assert _ws_header(ws) == [0] * 12
+    ref = _rank_gate_ref(hl, xb, params, 0.9) if hidden else oracle_y(hl, xb)
+    assert_close(gpu_y_f64(y, "f16"), ref, "wide, poll limit 0")
+    assert spear.spear_workspace_flags(ws) == (1 if one_launch else 0)
+    hdr = _ws_header(ws)
+    assert hdr[0] == 0 and hdr[2:] == [0] * 10
 
 
 def test_decode_wide_gate_off_is_rank_zero_bitwise():
