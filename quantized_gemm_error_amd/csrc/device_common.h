@@ -112,6 +112,14 @@ __device__ __forceinline__ void publish_wait() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Round to bf16 and the bf16 of the remainder: hi + lo equals v to a relative
+// 2^-16 (exactly when v has at most 16 significant bits, as fp16 values do).
+__device__ __forceinline__ void split_bf16(float v, uint16_t &hi, uint16_t &lo) {
+  const __bf16 h = (__bf16)v;
+  hi = bitcast<uint16_t>(h);
+  lo = bitcast<uint16_t>((__bf16)(v - (float)h));
+}
+
 // Per-row zero-point constant for dequant_word.
 //   fp16: packed pair of -(1024 + z) (exact: 1024 + z is an integer < 2048).
 //   bf16: 2^23 + z as an fp32 bit pattern.

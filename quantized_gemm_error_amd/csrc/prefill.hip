@@ -108,13 +108,6 @@ __device__ __forceinline__ f32x4_t split_sum4(const float *p, size_t stride, int
   return t;
 }
 
-// Round to bf16 and the bf16 of the remainder: hi + lo equals v to a relative
-// 2^-16 (exactly when v has at most 16 significant bits, as fp16 values do).
-__device__ __forceinline__ void split_bf16(float v, uint16_t &hi, uint16_t &lo) {
-  const __bf16 h = (__bf16)v;
-  hi = bitcast<uint16_t>(h);
-  lo = bitcast<uint16_t>((__bf16)(v - (float)h));
-}
 
 
 constexpr int kEpiRc = 32;           // ranks per epilogue chunk: the K of one 16x16x32 MFMA

@@ -83,6 +83,9 @@ constexpr int kMaxProducerSplits = 8;  // wide_producer_ksplit's largest count
 #ifndef SPEAR_WIDE_LOOKAHEAD128
 #define SPEAR_WIDE_LOOKAHEAD128 0
 #endif
+#ifndef SPEAR_WIDE_PROD_STEPS
+#define SPEAR_WIDE_PROD_STEPS 32  // 32-wide steps of K per producer split (before the 4..8 clamp)
+#endif
 #ifndef SPEAR_WIDE_FORCE_KSP
 #define SPEAR_WIDE_FORCE_KSP 0  // > 0: that many K-splits (or the nearest count with no empty split)
 #endif
@@ -149,34 +152,48 @@ __device__ __forceinline__ int tile_piece_off(const WideArgs &a, int q, int t, i
 __device__ void form_u(const WideArgs &a, int tid) {
   const size_t stride = (size_t)a.M * a.rp1;
   const int q4 = a.rp1 / 4;
+  const int items = a.M * q4;
   const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
       a.tp, (short)0, (int)(a.ks * stride * sizeof(float)), 0x00020000);
   const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
       a.U, (short)0, (int)(stride * sizeof(float)), 0x00020000);
-  for (int i = tid; i < a.M * q4; i += kThreads) {
-    const int m = i / q4, j = 4 * (i - m * q4);
-    f32x4_t v[kMaxProducerSplits];
-    float w[kMaxProducerSplits];
+  // kUItems items per thread and round, all their loads in flight together
+  // (one round at up to 64 tokens and rank 64)
+  constexpr int kUItems = 3;
+  for (int i0 = tid; i0 < items; i0 += kUItems * kThreads) {
+    f32x4_t v[kUItems][kMaxProducerSplits];
+    float w[kUItems][kMaxProducerSplits];
 #pragma unroll
-    for (int q = 0; q < kMaxProducerSplits; ++q) {
-      const int qq = min(q, a.ks - 1);
-      const int base = (int)((qq * stride + (size_t)m * a.rp1) * sizeof(float));
-      v[q] = load_partials4(tr, base + j * 4);
-      w[q] = bitcast<float>(__builtin_amdgcn_raw_buffer_load_b32(tr, base + a.rank * 4, 0, 16));
-    }
-    f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-    float z = 0.f;
+    for (int u = 0; u < kUItems; ++u) {
+      const int i = min(i0 + u * kThreads, items - 1);
+      const int m = i / q4, j = 4 * (i - m * q4);
 #pragma unroll
-    for (int q = 0; q < kMaxProducerSplits; ++q)
-      if (q < a.ks) {
-        t += v[q];
-        z += w[q];
+      for (int q = 0; q < kMaxProducerSplits; ++q) {
+        const int base = (int)((min(q, a.ks - 1) * stride + (size_t)m * a.rp1) * sizeof(float));
+        v[u][q] = load_partials4(tr, base + j * 4);
+        w[u][q] = bitcast<float>(__builtin_amdgcn_raw_buffer_load_b32(tr, base + a.rank * 4, 0, 16));
       }
-    const float g = gate_sigmoid(z + a.b_gate);
-    f32x4_t u;
+    }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) u[c] = (j + c < a.rank) ? g * t[c] : 0.f;
-    store_partials4(u, ur, (m * a.rp1 + j) * 4);
+    for (int u = 0; u < kUItems; ++u) {
+      const int i = i0 + u * kThreads;
+      if (i < items) {
+        const int m = i / q4, j = 4 * (i - m * q4);
+        f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+        float z = 0.f;
+#pragma unroll
+        for (int q = 0; q < kMaxProducerSplits; ++q)
+          if (q < a.ks) {
+            t += v[u][q];
+            z += w[u][q];
+          }
+        const float g = gate_sigmoid(z + a.b_gate);
+        f32x4_t uo;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) uo[c] = (j + c < a.rank) ? g * t[c] : 0.f;
+        store_partials4(uo, ur, (m * a.rp1 + j) * 4);
+      }
+    }
   }
 }
 
@@ -321,6 +338,12 @@ __device__ void finish_tile(const WideArgs &a, const f32x4_t (&acc)[R][MB], int 
   volatile int *vote = (volatile int *)((char *)lds + a.red_off);
   uint32_t counted = kNotCounted;
   f32x4_t v[R][MB];
+  // the first read of the producers' count, issued before the split sums
+  // are gathered so that the two round trips overlap (used by thread 0)
+  uint32_t seen = 0;
+  auto poll = [&]() {
+    return __hip_atomic_load(&a.hdr->arrive.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   if (a.ksp > 1) {
     const __amdgpu_buffer_rsrc_t pr =
         __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
@@ -341,6 +364,9 @@ __device__ void finish_tile(const WideArgs &a, const f32x4_t (&acc)[R][MB], int 
       if (EC && tid == 0) finish_after(a, count_out(a));
       return;
     }
+    // the first read of the producers' count goes out before the split
+    // sums' loads (a wait for it then covers no later load)
+    if (EC && tid == 0) seen = poll();
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -377,19 +403,49 @@ __device__ void finish_tile(const WideArgs &a, const f32x4_t (&acc)[R][MB], int 
   }
 
   if constexpr (EC) {
-    const int nst = (a.rank + 3) / 4;
-    // B for the first eight rank steps does not depend on the producers
-    float bv[R][8];
-    auto bload = [&](int st0) {
+    // U B^T in 32-rank chunks of bf16 16x16x32 MFMAs on hi/lo halves: u =
+    // u_hi + u_lo and b = b_hi + b_lo (exact for fp16 and bf16 B), the
+    // products u_hi b_hi + u_lo b_hi + u_hi b_lo accumulated in fp32, which
+    // leaves a relative error near 2^-17 in the compensator term.  A lane
+    // holds ranks 32 c + 8 h .. + 7 of its token (A operand) and of its
+    // output row (B operand); ranks past rank are zeros.
+    const int nch = (a.rank + 31) / 32;
+    if (a.ksp == 1 && tid == 0) seen = poll();  // before the B loads, as above
+    // all of this lane's B (it does not depend on the producers), loaded
+    // before the wait: 16-byte pieces when every row's piece is aligned
+    // (rank % 8 == 0 and B 16-byte aligned; a piece past rank then reads
+    // the row's first and is masked), else value by value
+    constexpr int kMaxChunks = (SPEAR_MAX_RANK + 31) / 32;
+    u16x8_t bq[kMaxChunks][R];
+    const bool bvec = (a.rank % 8) == 0 && ((uintptr_t)a.B % 16) == 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = min(4 * min(st0 + i, nst - 1) + h, a.rank - 1);
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < nch) {
+        const int j0 = 32 * c + 8 * h;
 #pragma unroll
-        for (int r = 0; r < R; ++r) bv[r][i] = to_f32<DT>(a.B[(size_t)row[r] * a.rank + j]);
+        for (int r = 0; r < R; ++r) {
+          const uint16_t *brow = a.B + (size_t)row[r] * a.rank;
+          if (bvec) {
+            bq[c][r] = *(const u16x8_t *)(brow + (j0 < a.rank ? j0 : 0));
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bq[c][r][i] = brow[min(j0 + i, a.rank - 1)];
+          }
+        }
+      }
+    auto split8 = [](const float (&f)[8], u32x4_t &hi, u32x4_t &lo) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t h0, l0, h1, l1;
+        split_bf16(f[2 * i], h0, l0);
+        split_bf16(f[2 * i + 1], h1, l1);
+        hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
       }
     };
-    bload(0);
-    __syncthreads();  // every wave is done with the staged x (the LDS takes U next)
+    // every wave is done with the staged x (the LDS takes U next); an
+    // LDS-only barrier, so the B loads stay in flight
+    lds_barrier();
     if (tid == 0) {
       int expired = 0;
       for (uint32_t it = 0;; ++it) {
@@ -398,14 +454,13 @@ __device__ void finish_tile(const WideArgs &a, const f32x4_t (&acc)[R][MB], int 
           __hip_atomic_fetch_or(&a.hdr->flags.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
-        if (__hip_atomic_load(&a.hdr->arrive.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-            (uint32_t)a.producers + 1u)
-          break;
+        if (seen >= (uint32_t)a.producers + 1u) break;
         __builtin_amdgcn_s_sleep(1);
+        seen = poll();
       }
       vote[1] = expired;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) counted = count_out(a);  // the count is read no more
     float *ul = (float *)lds;  // U [M][rp1]
     if (vote[1] == 0) {
@@ -417,20 +472,40 @@ __device__ void finish_tile(const WideArgs &a, const f32x4_t (&acc)[R][MB], int 
     } else {
       self_u<DT>(a, ul, tid);
     }
-    for (int st0 = 0; st0 < nst; st0 += 8) {
-      if (st0 > 0) bload(st0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = 4 * (st0 + i) + h;
-        if (st0 + i < nst) {
-          const bool jin = j < a.rank;
+    for (int c = 0; c < kMaxChunks; ++c) {
+      if (c >= nch) break;
+      u32x4_t bh[R], bl[R];
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const int m = col + 16 * mb;
-            const float u = (jin && m < a.M) ? ul[m * a.rp1 + j] : 0.f;
+      for (int r = 0; r < R; ++r) {
+        float f[8];
 #pragma unroll
-            for (int r = 0; r < R; ++r) v[r][mb] = mfma_16x16x4_f32(u, jin ? bv[r][i] : 0.f, v[r][mb]);
-          }
+        for (int i = 0; i < 8; ++i)
+          f[i] = (32 * c + 8 * h + i < a.rank) ? to_f32<DT>(bq[c][r][i]) : 0.f;
+        split8(f, bh[r], bl[r]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = col + 16 * mb;
+        // two unconditional 16-byte reads (past the row's rank they read
+        // the next row or the LDS beyond U, still inside the allocation),
+        // then zeros selected where j >= rank or m >= M: a read under the
+        // mask's condition would wait for each value on its own
+        const float *up = ul + min(m, a.M - 1) * a.rp1 + 32 * c + 8 * h;
+        const f32x4_t u0 = *(const f32x4_t *)up, u1 = *(const f32x4_t *)(up + 4);
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int j = 32 * c + 8 * h + i;
+          f[i] = (j < a.rank && m < a.M) ? (i < 4 ? u0[i] : u1[i - 4]) : 0.f;
+        }
+        u32x4_t ah, al;
+        split8(f, ah, al);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          v[r][mb] = mfma_16x16x32<DT_BF16>(ah, bh[r], v[r][mb]);
+          v[r][mb] = mfma_16x16x32<DT_BF16>(al, bh[r], v[r][mb]);
+          v[r][mb] = mfma_16x16x32<DT_BF16>(ah, bl[r], v[r][mb]);
         }
       }
     }
@@ -783,9 +858,12 @@ hipError_t launch_mb(const WideArgs &a, const WidePlan &p, bool ec, bool perch, 
   return launch_fused<DT, 8, 1>(a, grid, p.lds, ec, perch, p.fused, s);
 }
 
-// K-splits of the producers: about 2048 columns each, from 4 to 8.
+// K-splits of the producers: enough that each wave covers its split in one
+// round of loads (32 steps of 32 columns per workgroup), a multiple of 4 from
+// 4 to 8: under the consumers' weight stream every round trip of a producer
+// is long.
 int wide_producer_ksplit(int K) {
-  const int need = (K / 32 + 63) / 64;
+  const int need = (K / 32 + SPEAR_WIDE_PROD_STEPS - 1) / SPEAR_WIDE_PROD_STEPS;
   const int ks = (need + 3) / 4 * 4;
   return ks < 4 ? 4 : (ks > 8 ? 8 : ks);
 }
@@ -835,6 +913,10 @@ WidePlan plan_wide(const LayerDesc &L, int M) {
       p.nbs = nbs;
     }
   }
+  // fewer producer splits where consumers and producers would not all be
+  // resident at once (the last consumers would wait for a second round)
+  while (p.ks > 4 && p.n_tiles * p.ksp + p.rb_a * p.ks > 256) p.ks -= 4;
+  p.producers = p.rb_a * p.ks;
   p.direct = L.rank == 0 && p.ksp == 1;
   // One launch finishes the tiles (the K-splits' sums through the tile
   // counters, the scalar gate's U from the last producer); the per-rank gate

@@ -232,6 +232,7 @@ WIDE_CASES = [
     (300, 2048, 0, 24, 90, "bf16", True, 8),      # per-rank gate, 128-token kernel
     (33000, 256, 128, 16, 40, "f16", False, 0),   # 129 tiles: more than the tile counters, no K split
     (16512, 4096, 128, 16, 64, "f16", False, 0),  # 129 tiles with K-splits: the three-launch form
+    (520, 1024, 128, 20, 64, "f16", True, 0),     # rank % 8 != 0: B read value by value
 ]
 
 
