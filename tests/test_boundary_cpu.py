@@ -274,6 +274,23 @@ def test_plan_dispatch_and_errors(lib):
     assert _plan(lay0, 100, 0)["workspace_bytes"] == 0
 
 
+def test_prefill_plan_counts_the_split_gemm_producers(lib):
+    """A K-split prefill GEMM with the scalar gate and K <= 16384 carries the compensator's
+    producers in its launch (32-token blocks x at most 8 K-splits, padded to a multiple of 8
+    workgroups ahead of the tiles); with K past 16384, the per-rank gate, an unsplit GEMM or
+    rank 0 it has none."""
+    def plan(M=100, **kw):
+        lay = _layer(**kw)
+        return _plan(lay, M, lib.spear_workspace_bytes(ctypes.byref(lay), M), "prefill")
+    p = plan(N=512, K=2048, group_size=128, rank=32)
+    assert p["k_splits"] > 1 and p["producers"] == 4 * 8            # 4 token blocks x 8 splits
+    p0 = plan(N=512, K=2048, group_size=128, rank=0, A=None, B=None, w_gate=None)
+    assert p0["producers"] == 0 and p["workgroups"] == p0["workgroups"] + 32
+    assert plan(N=256, K=16640, group_size=128, rank=16)["producers"] == 0
+    big = plan(M=2048, N=8192, K=4096, group_size=128, rank=32)
+    assert big["k_splits"] == 1 and big["producers"] == 0
+
+
 def test_dispatch_splits_off_a_short_decode_tail(lib):
     """spear_linear gives the last r = M mod 128 tokens to the decode path when 1 <= r <= 32,
     at least eight full 128-token tile rows precede them, r is within the decode threshold

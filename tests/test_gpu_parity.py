@@ -640,6 +640,36 @@ def test_prefill_ragged_tail(N, K, G, r, M, dtype):
     assert_close(gpu_y_f64(y, dtype)[:, rows], oracle_y(hl, xb, rows=rows), f"tail {M} rows")
 
 
+# K-split GEMMs with the scalar gate: up to K = 16384 the compensator's producers run inside
+# the split GEMM launch and the producer that completes each 32-token block forms its U rows
+# (two launches, either schedule); past it the compensator and U kernels come first.
+SPROD_CASES = [
+    # N, K, G, r, M, dtype, aux
+    (512, 2048, 128, 32, 100, "f16", False),   # producers in the split GEMM launch, serial
+    (512, 2048, 0, 64, 257, "bf16", True),     # the same, concurrent schedule, ragged token block
+    (256, 16640, 128, 16, 64, "f16", False),   # K past 16384: four launches
+]
+
+
+@pytest.mark.parametrize("N,K,G,r,M,dtype,aux", SPROD_CASES)
+def test_prefill_split_gemm_compensator(N, K, G, r, M, dtype, aux):
+    """A K-split GEMM with the scalar gate matches the oracle in both forms, and the
+    token-block counters the two-launch form uses are back at zero with no flag set."""
+    note(f"prefill split N={N} K={K} G={G} r={r} M={M} {dtype} aux={aux}")
+    hl, xb, lay, x = _setup(N, K, G, r, seed=N + K + M + 7, dtype=dtype, M=M, outliers=True,
+                            b_gate=0.25)
+    ws = spear.new_workspace(lay, M)
+    plan = spear.spear_linear_plan(lay, M, ws.numel(), "prefill")
+    assert plan["k_splits"] > 1
+    assert (plan["producers"] > 0) == (K <= 16384)
+    y = spear.spear_linear_prefill(lay, x, workspace=ws,
+                                   aux_stream=torch.cuda.Stream() if aux else None)
+    torch.cuda.synchronize()
+    assert_close(gpu_y_f64(y, dtype), oracle_y(hl, xb), f"prefill split {N}x{K} M={M}")
+    assert spear.spear_workspace_flags(ws) == 0
+    assert _ws_header(ws) == [0] * 12
+
+
 FUSED_CASES = [
     # N, K, G, r, M, dtype: unsplit GEMMs, scalar gate (the producers run inside the GEMM launch)
     (300, 768, 128, 32, 200, "f16"),    # ragged N and M tiles
