@@ -242,8 +242,13 @@ spear_status_t spear_linear_decode_noalloc(const spear_layer_t *layer, spear_dty
  *     see spear_set_decode_spin_limit) before its epilogue and computes the
  *     sums of its own tokens if the wait expires (bit 0 of the workspace
  *     flags).  aux_stream is then not used.  Otherwise (per-rank gate, or a
- *     K-split GEMM at few tiles) the compensator kernels run on aux_stream
- *     beside the GEMM and a finish kernel adds their term after the join.
+ *     K-split GEMM at few tiles with K > 16384) the compensator kernels run on
+ *     aux_stream beside the GEMM and a finish kernel adds their term after
+ *     the join.
+ * In both schedules, a K-split GEMM (few output tiles) with the scalar gate
+ * and K <= 16384 runs as two launches on main_stream: the compensator's
+ * producers inside the GEMM launch, ahead of its tiles, and a finish kernel
+ * that sums the splits and adds the compensator's term.
  * When the call returns, work on aux_stream is ordered after main_stream's
  * prior work and main_stream's later work is ordered after all of it.
  */

@@ -38,9 +38,13 @@
 //    from the sums exactly as prefill_u_kernel does (or, if the wait
 //    expires, computes its tokens' sums itself) and adds U B^T before y is
 //    rounded once.  The last workgroup to finish resets the counters.  With
-//    the per-rank gate or a K-split GEMM the compensator kernels run on the
-//    aux stream beside the GEMM, and after the join the finish kernel adds
-//    U B^T.
+//    the per-rank gate or a K-split GEMM past K = 16384 the compensator
+//    kernels run on the aux stream beside the GEMM, and after the join the
+//    finish kernel adds U B^T;
+//  * either schedule, a K-split GEMM with the scalar gate up to K = 16384
+//    (SPROD): the producers run in the split GEMM launch ahead of its tiles,
+//    the producer that completes each 32-token block forms that block's U
+//    rows, and the finish kernel (the next launch) adds U B^T.
 #include <algorithm>
 #include <mutex>
 #include <unordered_map>
