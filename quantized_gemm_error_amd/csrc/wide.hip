@@ -921,12 +921,8 @@ WidePlan plan_wide(const LayerDesc &L, int M) {
   // One launch finishes the tiles (the K-splits' sums through the tile
   // counters, the scalar gate's U from the last producer); the per-rank gate
   // keeps its U kernel and the finish kernel, as do K-split calls with more
-  // tiles than the header has counters.  Measured: at 128 tokens with the
-  // compensator and three or more K-splits the two extra launches are
-  // faster (the tile's one finishing workgroup then adds U B^T for 128 tokens
-  // after its main loop, where the finish kernel spreads that work).
-  p.fused = !p.direct && L.rg_hidden == 0 && (p.ksp == 1 || p.n_tiles <= kMaxSplitTiles) &&
-            !(L.rank > 0 && p.mb == 8 && p.ksp >= 3);
+  // tiles than the header has counters.
+  p.fused = !p.direct && L.rg_hidden == 0 && (p.ksp == 1 || p.n_tiles <= kMaxSplitTiles);
   p.buf_halves = 16 * p.mb * kXStr;
   // up to 64 tokens the staged chunks alternate between two buffers
   p.red_off = (int)round256((size_t)p.buf_halves * 2 * (p.mb <= 4 ? 2 : 1));

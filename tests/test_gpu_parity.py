@@ -261,15 +261,15 @@ def test_decode_wide_parity(N, K, G, r, M, dtype, outl, hidden):
     (700, 2048, 48, 0, True),     # 8 K-splits, 64-token kernel
     (3000, 512, 100, 0, True),    # 2 K-splits, 128-token kernel
     (8192, 512, 100, 0, True),    # no K-split: every workgroup finishes its tile
-    (700, 2048, 100, 0, False),   # 8 K-splits at 128 tokens: U and finish launches
+    (700, 2048, 100, 0, True),    # 8 K-splits, 128-token kernel
     (700, 2048, 48, 8, False),    # per-rank gate: U and finish launches
 ])
 def test_decode_wide_wait_expiry(N, K, M, hidden, one_launch):
     """With no wait at all for the producers (poll limit 0, set on the host), the one-launch
     wide form computes U itself in every workgroup that finishes a tile: the output still
     matches the oracle, bit 0 of the workspace flags records the expiry and the counters are
-    back at zero.  The three-launch form (per-rank gate; the compensator at 128 tokens with
-    three or more K-splits) has no wait and sets no flag.  Every kernel exits normally."""
+    back at zero.  The per-rank gate's three-launch form has no wait and sets no flag.  Every
+    kernel exits normally."""
     note(f"decode wide, poll limit 0, N={N} K={K} M={M} hidden={hidden}")
     hl, xb, lay, x = _setup(N, K, 128, 32, seed=M + 3, M=M, outliers=True, b_gate=0.3)
     params = None
