@@ -272,7 +272,7 @@ struct GemmArgs {
   const uint16_t *x;
   uint16_t *y;
   int N, K, G, ngroups, M;
-  UView u;            // EPI: U, complete before the launch
+  UView u;            // EPI: U, complete before the launch; SPROD: where the producers form U
   const uint16_t *B;  // EPI: [N][rank]
   int ks;             // SPLIT: K splits (blockIdx.z), each a contiguous range of k-blocks
   float *part;        // SPLIT: [ks][M][N] fp32 partial outputs

@@ -10,8 +10,7 @@
 // tokens and K = 8192) must be reused across many output rows, which the
 // small-M decode kernels (16 to 64 rows per workgroup, each staging all of
 // x) do not do, and the K-splits that fill the chip need their partial sums
-// reduced.  Here the call is three stream-ordered launches, with no
-// workgroup ever waiting on another:
+// reduced.
 //
 //  * wide_kernel: consumer workgroups of 8 waves own a tile of 128 R output
 //    rows (R 16-row blocks per wave) and one of ksp K-splits.  x for the
@@ -19,12 +18,18 @@
 //    keeps the next four 128-wide blocks of its rows' packed nibbles in
 //    flight; each staged x fragment feeds R row blocks of 16x16x32 MFMAs and
 //    each dequantized weight word (exact, in registers) feeds every token
-//    block.  They store fp32 partial outputs [ksp][M][N] (or, at rank 0 with
-//    one split, round y directly).  Producer workgroups in the same launch
-//    store the K-split sums of [A; w_g] x for every token;
-//  * the compensator's U = g (A x) formed once from those sums, and
-//  * the finish kernel (both shared with the prefill path), which sums the
-//    partials in split order, adds U B^T and rounds y once.
+//    block.  Producer workgroups in the same launch compute the K-split sums
+//    of [A; w_g] x for every token.
+//  * One launch (FUSED, the scalar gate): the producer that completes the
+//    producers' count forms U = g (A x); the K-split that completes a tile's
+//    count sums the tile's partials in split order, waits (bounded) for U,
+//    adds U B^T and rounds y once (finish_tile).  At rank 0 with one split
+//    every workgroup rounds its own y.
+//  * Three launches (the per-rank gate, or K-splits over more tiles than the
+//    workspace header has counters): the consumers store fp32 partial
+//    outputs [ksp][M][N], then the compensator's U is formed once, then the
+//    finish kernel (both shared with the prefill path) sums the partials in
+//    split order, adds U B^T and rounds y once.
 //
 // Every loop that touches memory has a compile-time shape, so its waits
 // count its loads exactly.
