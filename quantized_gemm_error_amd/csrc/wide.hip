@@ -65,8 +65,14 @@ __host__ __device__ constexpr int xplace(int p) {
 constexpr int kMaxLds = 160 * 1024;
 constexpr int kMaxProducerSplits = 8;  // wide_producer_ksplit's largest count
 // Launch-shape constants of plan_wide (measured on MI355X).
-#ifndef SPEAR_WIDE_R64
-#define SPEAR_WIDE_R64 1  // 16-row blocks per wave at up to 64 tokens
+#ifndef SPEAR_WIDE_R2_MIN_TILES
+// Two 16-row blocks per wave (256-row tiles: half the LDS fragment reads per
+// MFMA and half the x staging per weight byte) at up to 64 tokens for
+// per-channel layers with at least this many such tiles; measured at 64
+// tokens: 8192 -> 28672 (112 tiles) 44.6 against 48.0 us, 8192^2 (32 tiles,
+// which then needs twice the K-splits) 27.9 against 22.8 us.  The group-wise
+// kernel spills at two blocks.
+#define SPEAR_WIDE_R2_MIN_TILES 96
 #endif
 #ifndef SPEAR_WIDE_WG_RATE
 #define SPEAR_WIDE_WG_RATE 25e9  // bytes/s of weights one workgroup streams
@@ -889,7 +895,7 @@ WidePlan plan_wide(const LayerDesc &L, int M) {
   p.ok = false;
   if (M < 1 || M > 128) return p;
   p.mb = M <= 64 ? 4 : 8;
-  p.r = p.mb == 4 ? SPEAR_WIDE_R64 : 1;
+  p.r = (p.mb == 4 && L.per_channel && (L.N + 255) / 256 >= SPEAR_WIDE_R2_MIN_TILES) ? 2 : 1;
   p.rb_a = L.rank > 0 ? (L.rank + L.gate_rows() + 15) / 16 : 0;
   p.ks = L.rank > 0 ? wide_producer_ksplit(L.K) : 0;
   p.producers = p.rb_a * p.ks;

@@ -233,6 +233,7 @@ WIDE_CASES = [
     (33000, 256, 128, 16, 40, "f16", False, 0),   # 129 tiles: more than the tile counters, no K split
     (16512, 4096, 128, 16, 64, "f16", False, 0),  # 129 tiles with K-splits: the three-launch form
     (520, 1024, 128, 20, 64, "f16", True, 0),     # rank % 8 != 0: B read value by value
+    (24576, 1024, 0, 16, 48, "bf16", True, 0),    # per-channel, 96 256-row tiles: two row blocks a wave
 ]
 
 
