@@ -135,7 +135,7 @@ typedef struct spear_layer {
 
 #define SPEAR_MAX_RANK 128
 #define SPEAR_MAX_K 131072
-#define SPEAR_MAX_DECODE_M 128  /* 1..32: per-row-group kernels; 33..128: the wide-tile kernel */
+#define SPEAR_MAX_DECODE_M 128  /* 1..32: per-row-group kernels (but see below); 33..128: the wide-tile kernel */
 
 /*
  * Workspace bytes that spear_linear_decode, spear_linear_prefill and
@@ -189,9 +189,15 @@ spear_status_t spear_tile_int4(const int32_t *words, int32_t *qweight, int64_t N
  * tiles of 128 output rows over a K-split each and stream x through LDS, so
  * that each staged activation fragment feeds many rows, and the last split to
  * finish a tile sums its partials in split order and adds the compensator.
- * (From 33 tokens, with the per-rank gate, or with K-splits over more than
- * 128 tiles, two more launches on the same stream do that: one forms the
- * compensator's gated sums, a finish kernel adds them and the partials.)
+ * The tile launch also serves 17..32 tokens on layers of at most 64 tiles of
+ * 128 rows for which the split thresholds below want a K-split but no
+ * split-K launch shape fits (long K with group-wise scales, e.g. K = 16384 at
+ * G = 128, or a rank-64 compensator at K = 8192 past 16 tokens); there the
+ * whole-K row groups would each stream all of x.  spear_linear_plan reports
+ * which launch a call takes.  (With the tile launch: with the per-rank
+ * gate, or with K-splits over more than 128 tiles, two more launches on the
+ * same stream do that: one forms the compensator's gated sums, a finish
+ * kernel adds them and the partials.)
  * x [M][K] and y [M][N] are row-major activation-type device arrays, x and y
  * 16-byte aligned.  The gate, A x and the gated B (A x) term are computed in
  * the same launch as the 4-bit product and added before y is rounded.
@@ -360,7 +366,7 @@ typedef enum spear_path {
   SPEAR_PATH_DECODE = 1,        /* fused decode, one workgroup per group of output rows */
   SPEAR_PATH_DECODE_SPLIT = 2,  /* fused decode, K split across each 128-row tile's workgroups */
   SPEAR_PATH_PREFILL = 3,       /* the prefill GEMM path */
-  SPEAR_PATH_DECODE_WIDE = 4,   /* fused decode for 33..128 tokens: 128-row tiles over K-splits */
+  SPEAR_PATH_DECODE_WIDE = 4,   /* fused decode with 128-row tiles over K-splits: 33..128 tokens (and 17..32 on long-K layers) */
   SPEAR_PATH_PREFILL_DECODE_TAIL = 5 /* spear_linear only: prefill for M - r tokens, then decode for
                                         the last r (the plan describes the prefill launch) */
 } spear_path_t;

@@ -17,6 +17,10 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 constexpr int32_t kSmallDecodeM = 32;  // the per-row-group decode kernels; past it, the wide one
+// Layers of at most this many 128-row tiles take the wide launch at 17..32
+// tokens where the split-K decode launch is wanted but does not fit
+// (small_decode).
+constexpr int kWideLongKMaxTiles = 64;
 // spear_linear's dispatch threshold.  Measured on MI355X (compensated calls):
 // at 64 tokens the wide decode launch beats the prefill path on every Llama-7B
 // and Llama-70B projection (e.g. 8192 x 8192: 36.7 vs 49.8 us; 8192 -> 28672:
@@ -132,13 +136,32 @@ spear_status_t hip_status(hipError_t e, const char *what) {
   return ok();
 }
 
+// Whether decode for M tokens takes the per-row-group kernels (else the
+// wide launch).  Up to 32 tokens it does, except past 16 tokens (two token
+// blocks) where the column threshold wants the split-K launch but no split
+// fits (the group-wise scale staging caps a split's length, and the
+// compensator's LDS at rank 64) and the layer has at most 64 tiles of 128
+// rows.  There the unsplit launch has few workgroups, each streaming all of
+// x through its LDS along the whole of K, while the wide launch splits K
+// over 128-row tiles.  Measured at 17..32 tokens (fp16, graph-replayed):
+// 16384->4096 20-27% and 28672->4096 35-38% faster, 28672->8192 15-17%
+// rank 0 and 1-30% compensated; with more tiles the unsplit launch fills
+// the chip and stays ahead (16384->16384: wide 15-22% slower, 8192->28672
+// rank 0 13% slower).  The rule reads the layer's shape, rank and M only.
+bool small_decode(const LayerDesc &d, int M) {
+  if (M > kSmallDecodeM) return false;
+  if (M <= 16 || !decode_split_wanted(M, d.K) || decode_split_fits(d, M)) return true;
+  if ((d.N + 127) / 128 > kWideLongKMaxTiles) return true;
+  return !plan_wide(d, M).ok;
+}
+
 // Decode for M tokens (1..SPEAR_MAX_DECODE_M): whether a launch shape fits,
 // the least workspace, and the launch.
 bool decode_fits(const LayerDesc &d, int M) {
-  return M <= kSmallDecodeM ? decode_supported(d, M) : plan_wide(d, M).ok;
+  return small_decode(d, M) ? decode_supported(d, M) : plan_wide(d, M).ok;
 }
 size_t decode_need(const LayerDesc &d, int M) {
-  return M <= kSmallDecodeM ? decode_workspace_bytes(d, M) : wide_workspace_bytes(d, M);
+  return small_decode(d, M) ? decode_workspace_bytes(d, M) : wide_workspace_bytes(d, M);
 }
 
 // The decode tail of a prefill-sized call (prefill_decode_tail), when the
@@ -152,7 +175,7 @@ int dispatch_decode_tail(const LayerDesc &d, int M, void *workspace, size_t work
 }
 hipError_t decode_launch(const LayerDesc &d, int dtype, const void *x, void *y, int M, void *ws,
                          size_t ws_bytes, hipStream_t s) {
-  if (M <= kSmallDecodeM)
+  if (small_decode(d, M))
     return launch_decode(d, dtype, (const uint16_t *)x, (uint16_t *)y, M, ws, ws_bytes, s);
   return launch_wide(d, dtype, (const uint16_t *)x, (uint16_t *)y, M, ws, s);
 }
@@ -215,7 +238,7 @@ size_t spear_workspace_bytes(const spear_layer_t *layer, int32_t M) {
   size_t need = prefill_workspace_bytes(d, M < 1 ? 1 : M);
   const int dm = M < 1 ? 1 : (M < SPEAR_MAX_DECODE_M ? M : SPEAR_MAX_DECODE_M);
   for (int m = 1; m <= dm; ++m) {  // the split launches' needs vary with M's tile plan
-    const size_t dec = m <= kSmallDecodeM ? decode_fast_workspace_bytes(d, m)
+    const size_t dec = small_decode(d, m) ? decode_fast_workspace_bytes(d, m)
                                           : wide_workspace_bytes(d, m);
     if (dec > need) need = dec;
   }
@@ -356,7 +379,7 @@ spear_status_t spear_linear_plan(const spear_layer_t *layer, int32_t M, size_t w
     if (!decode_fits(d, M))
       return fail(SPEAR_ERR_UNSUPPORTED, "no decode launch shape fits K=%d G=%d M=%d", d.K, d.G, M);
     if ((st = check_ws(ws, workspace_bytes, decode_need(d, M))) != SPEAR_OK) return st;
-    if (M <= kSmallDecodeM)
+    if (small_decode(d, M))
       describe_decode(d, M, workspace_bytes, plan);
     else
       describe_wide(d, M, plan);

@@ -55,6 +55,10 @@ int get_decode_split_min_m() { return g_split_min_m.load(); }
 void set_decode_split_min_k(int k) { g_split_min_k.store(k); }
 int get_decode_split_min_k() { return g_split_min_k.load(); }
 
+bool decode_split_fits(const LayerDesc &L, int M) {
+  return (four_waves(L, M) ? w4::plan_decode_split(L, M) : w8::plan_decode_split(L, M)).ok;
+}
+
 bool decode_supported(const LayerDesc &L, int M) {
   return four_waves(L, M) ? w4::decode_supported(L, M) : w8::decode_supported(L, M);
 }

@@ -103,6 +103,7 @@ bool decode_supported(const LayerDesc &L, int M);
 size_t decode_workspace_bytes(const LayerDesc &L, int M);       // required
 size_t decode_fast_workspace_bytes(const LayerDesc &L, int M);  // enough for the split-K launch
 bool decode_split_wanted(int M, int K);  // the token and column thresholds (decode.hip)
+bool decode_split_fits(const LayerDesc &L, int M);  // a split-K launch shape exists
 void set_decode_split_min_m(int m);
 int get_decode_split_min_m();
 void set_decode_split_min_k(int k);

@@ -345,6 +345,34 @@ def test_graph_calls_reject_null_handles(lib):
     assert lib.spear_graph_destroy(None) == 0
 
 
+def test_decode_routes_long_k_to_wide_past_16_tokens(lib):
+    """17..32 tokens take the wide launch where the column threshold wants the split-K launch,
+    no split fits and the layer has at most 64 row tiles of 128; everywhere else below 33
+    tokens the row-group kernels (split or not) serve the call."""
+    def path(M, **kw):
+        lay = _layer(**kw)
+        return _plan(lay, M, lib.spear_workspace_bytes(ctypes.byref(lay), M), "decode")["path"]
+    for r in (32, 0):
+        for M in (17, 24, 32):
+            assert path(M, N=4096, K=16384, group_size=128, rank=r) == "decode_wide"
+            assert path(M, N=520, K=16384, group_size=128, rank=r) == "decode_wide"
+            assert path(M, N=16384, K=16384, group_size=128, rank=r) == "decode"      # 128 tiles
+            assert path(M, N=4096, K=11008, group_size=128, rank=r) == "decode_split"  # fits
+            assert path(M, N=4096, K=4096, group_size=128, rank=r) == "decode"   # no split wanted
+        assert path(16, N=4096, K=16384, group_size=128, rank=r) == "decode"
+        assert path(1, N=4096, K=16384, group_size=128, rank=r) == "decode"
+    # the rank-64 compensator's LDS leaves no split at 8192 x 8192 past 16 tokens; rank 0 splits
+    assert path(17, N=8192, K=8192, group_size=8192, rank=64) == "decode_split"
+    assert path(32, N=8192, K=8192, group_size=8192, rank=64) == "decode_wide"
+    assert path(32, N=8192, K=8192, group_size=8192, rank=0) == "decode_split"
+    # with the split switched off by its token threshold, nothing is routed
+    assert lib.spear_set_decode_split_min_m(33) == 0
+    try:
+        assert path(32, N=4096, K=16384, group_size=128, rank=32) == "decode"
+    finally:
+        assert lib.spear_set_decode_split_min_m(16) == 0
+
+
 @pytest.mark.parametrize("K,N,G,r", [(8192, 8192, 8192, 64), (8192, 28672, 8192, 64),
                                      (28672, 8192, 28672, 64), (4096, 4096, 128, 32),
                                      (11008, 4096, 128, 32), (512, 512, 512, 16), (640, 300, 128, 24)])

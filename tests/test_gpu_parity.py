@@ -234,6 +234,10 @@ WIDE_CASES = [
     (16512, 4096, 128, 16, 64, "f16", False, 0),  # 129 tiles with K-splits: the three-launch form
     (520, 1024, 128, 20, 64, "f16", True, 0),     # rank % 8 != 0: B read value by value
     (24576, 1024, 0, 16, 48, "bf16", True, 0),    # per-channel, 96 256-row tiles: two row blocks a wave
+    # 17..32 tokens at long K where no split-K decode launch fits (few row tiles)
+    (520, 16384, 128, 32, 17, "f16", True, 0),    # 17 tokens: 47 padding rows in the 64-token tile
+    (1000, 16384, 128, 20, 32, "bf16", False, 0),
+    (700, 16640, 128, 32, 24, "f16", True, 8),    # per-rank gate: the three-launch form
 ]
 
 
