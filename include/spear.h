@@ -149,7 +149,11 @@ typedef struct spear_layer {
  * need different workspaces.
  *
  * Compensated layers need a workspace for every call.  For a layer with
- * r == 0 it is optional: prefill uses it to split K across workgroups when
+ * r == 0 it is optional, except for decode calls that take the tile launch
+ * with K-splits (spear_linear_plan: SPEAR_PATH_DECODE_WIDE, k_splits > 1),
+ * whose partial tiles it holds; a rank-0 layer's size can exceed that of a
+ * compensated layer of the same shape, whose producers may leave its tiles
+ * fewer K-splits.  Otherwise prefill uses it to split K across workgroups when
  * the output has few 128 x 128 tiles (small M), and decode uses it to
  * split K across the workgroups of each 128-row output tile where the
  * thresholds of spear_set_decode_split_min_m and _min_k ask for that.  Decode takes that split launch

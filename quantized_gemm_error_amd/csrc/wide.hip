@@ -927,6 +927,23 @@ WidePlan plan_wide(const LayerDesc &L, int M) {
   // fewer producer splits where consumers and producers would not all be
   // resident at once (the last consumers would wait for a second round)
   while (p.ks > 4 && p.n_tiles * p.ksp + p.rb_a * p.ks > 256) p.ks -= 4;
+  // If even the fewest producer splits leave no room (the tiles' splits alone
+  // take every slot), the tiles get the largest K-split count that does,
+  // and the producers their splits again.  At 28672 -> 8192, 17 and 24
+  // tokens, rank 64: 4 splits and 20 producers (276 workgroups) ran 66.7 /
+  // 70.4 us, 3 splits and 40 producers (232) 56.1 / 56.2 us.
+  if (SPEAR_WIDE_FORCE_KSP == 0 && p.rb_a > 0 && p.n_tiles * p.ksp + p.rb_a * p.ks > 256) {
+    for (int ks = p.ksp - 1; ks >= 1; --ks) {
+      const int nbs = (p.nb + ks - 1) / ks;
+      if ((p.nb + nbs - 1) / nbs != ks) continue;  // no empty split
+      if (p.n_tiles * ks + p.rb_a * 4 > 256) continue;
+      p.ksp = ks;
+      p.nbs = nbs;
+      p.ks = wide_producer_ksplit(L.K);
+      while (p.ks > 4 && p.n_tiles * p.ksp + p.rb_a * p.ks > 256) p.ks -= 4;
+      break;
+    }
+  }
   p.producers = p.rb_a * p.ks;
   p.direct = L.rank == 0 && p.ksp == 1;
   // One launch finishes the tiles (the K-splits' sums through the tile

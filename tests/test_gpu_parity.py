@@ -891,14 +891,15 @@ def test_llama7b_prefill_sampled(K, N, schedule):
 @pytest.mark.parametrize("K,N", synth.LLAMA70B_SHAPES)
 def test_llama70b_layer_sampled(K, N):
     """Every Llama-70B projection (per-channel, rank 64, fp16) at the token counts the bench
-    times (1, 64, 256) and at 2 and 4 (the long-K split-K decode launch), through the
+    times (1, 64, 256), at 2 and 4 (the long-K split-K decode launch) and at 17 and 32 (the
+    wide launch where no split-K decode launch fits, one round of workgroups), through the
     phase-aware entry point; prefill in both schedules.  After each call the workspace's
     flags and counters are back at zero."""
     w = synth.WORKLOADS["llama70b-layer"]
     hl = synth.make_layer(N, K, w["group_size"], w["rank"], seed=w["seed"] + K + N, dtype="f16")
     lay = spear.layer_to_device(hl, DEV)
     rows = sample_rows(N, 96, seed=70 + K)
-    for M in (1, 2, 4) + tuple(m for m in w["tokens"] if m > 1):
+    for M in (1, 2, 4, 17, 32) + tuple(m for m in w["tokens"] if m > 1):
         xb = synth.make_activations(M, K, seed=w["seed"] + M)
         x = spear.act_to_device(xb, "f16", DEV)
         ws = spear.new_workspace(lay, M)
