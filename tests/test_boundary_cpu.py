@@ -354,13 +354,17 @@ def test_decode_routes_long_k_to_wide_past_16_tokens(lib):
         return _plan(lay, M, lib.spear_workspace_bytes(ctypes.byref(lay), M), "decode")["path"]
     for r in (32, 0):
         for M in (17, 24, 32):
-            assert path(M, N=4096, K=16384, group_size=128, rank=r) == "decode_wide"
-            assert path(M, N=520, K=16384, group_size=128, rank=r) == "decode_wide"
-            assert path(M, N=16384, K=16384, group_size=128, rank=r) == "decode"      # 128 tiles
+            assert path(M, N=4096, K=28672, group_size=128, rank=r) == "decode_wide"
+            assert path(M, N=520, K=28672, group_size=128, rank=r) == "decode_wide"
             assert path(M, N=4096, K=11008, group_size=128, rank=r) == "decode_split"  # fits
             assert path(M, N=4096, K=4096, group_size=128, rank=r) == "decode"   # no split wanted
-        assert path(16, N=4096, K=16384, group_size=128, rank=r) == "decode"
-        assert path(1, N=4096, K=16384, group_size=128, rank=r) == "decode"
+        assert path(32, N=4096, K=16384, group_size=128, rank=r) == "decode_wide"
+        assert path(17, N=4096, K=16384, group_size=128, rank=r) == "decode_split"  # fits
+        assert path(32, N=16384, K=16384, group_size=128, rank=r) == "decode"  # 128 tiles
+        assert path(1, N=4096, K=28672, group_size=128, rank=r) == "decode"
+    # long splits with group-wise scales: up to 32 scale groups a split (two staging rounds)
+    assert path(16, N=4096, K=16384, group_size=128, rank=32) == "decode_split"
+    assert path(4, N=4096, K=28672, group_size=128, rank=32) == "decode_split"
     # the rank-64 compensator's LDS leaves no split at 8192 x 8192 past 16 tokens; rank 0 splits
     assert path(17, N=8192, K=8192, group_size=8192, rank=64) == "decode_split"
     assert path(32, N=8192, K=8192, group_size=8192, rank=64) == "decode_wide"
@@ -368,7 +372,7 @@ def test_decode_routes_long_k_to_wide_past_16_tokens(lib):
     # with the split switched off by its token threshold, nothing is routed
     assert lib.spear_set_decode_split_min_m(33) == 0
     try:
-        assert path(32, N=4096, K=16384, group_size=128, rank=32) == "decode"
+        assert path(32, N=4096, K=28672, group_size=128, rank=32) == "decode"
     finally:
         assert lib.spear_set_decode_split_min_m(16) == 0
 

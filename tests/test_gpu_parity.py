@@ -149,6 +149,8 @@ DECODE_CASES = [
     (160, 1024, 128, 128, 32, "f16", True),  # the largest rank (9 row blocks of [A; w_g]), 2 token blocks
     (64, 512, 0, 128, 1, "bf16", False),     # the largest rank at one token
     (48, 20480, 0, 8, 4, "f16", True),       # K past 16384: producer splits capped, two passes per wave
+    (300, 16384, 128, 32, 16, "f16", True),  # split-K with 17 scale groups a split: two staging rounds
+    (200, 28672, 128, 20, 4, "bf16", False), # 29 scale groups a split
 ]
 
 
@@ -235,9 +237,9 @@ WIDE_CASES = [
     (520, 1024, 128, 20, 64, "f16", True, 0),     # rank % 8 != 0: B read value by value
     (24576, 1024, 0, 16, 48, "bf16", True, 0),    # per-channel, 96 256-row tiles: two row blocks a wave
     # 17..32 tokens at long K where no split-K decode launch fits (few row tiles)
-    (520, 16384, 128, 32, 17, "f16", True, 0),    # 17 tokens: 47 padding rows in the 64-token tile
+    (520, 28672, 128, 32, 17, "f16", True, 0),    # 17 tokens: 47 padding rows in the 64-token tile
     (1000, 16384, 128, 20, 32, "bf16", False, 0),
-    (700, 16640, 128, 32, 24, "f16", True, 8),    # per-rank gate: the three-launch form
+    (700, 16640, 128, 32, 32, "f16", True, 8),    # per-rank gate: the three-launch form
 ]
 
 
