@@ -195,7 +195,7 @@ spear_status_t spear_tile_int4(const int32_t *words, int32_t *qweight, int64_t N
  * finish a tile sums its partials in split order and adds the compensator.
  * The tile launch also serves 17..32 tokens on layers of at most 64 tiles of
  * 128 rows for which the split thresholds below want a K-split but no
- * split-K launch shape fits (long K with group-wise scales, e.g. K = 16384 at
+ * split-K launch shape fits (long K with group-wise scales, e.g. K = 28672 at
  * G = 128, or a rank-64 compensator at K = 8192 past 16 tokens); there the
  * whole-K row groups would each stream all of x.  spear_linear_plan reports
  * which launch a call takes.  (With the tile launch: with the per-rank

@@ -139,13 +139,14 @@ spear_status_t hip_status(hipError_t e, const char *what) {
 // Whether decode for M tokens takes the per-row-group kernels (else the
 // wide launch).  Up to 32 tokens it does, except past 16 tokens (two token
 // blocks) where the column threshold wants the split-K launch but no split
-// fits (the group-wise scale staging caps a split's length, and the
-// compensator's LDS at rank 64) and the layer has at most 64 tiles of 128
+// fits (two token blocks of a long split's x with its scale table, or with a
+// rank-64 compensator's sums, overflow the LDS) and the layer has at most 64 tiles of 128
 // rows.  There the unsplit launch has few workgroups, each streaming all of
 // x through its LDS along the whole of K, while the wide launch splits K
-// over 128-row tiles.  Measured at 17..32 tokens (fp16, graph-replayed):
-// 16384->4096 20-27% and 28672->4096 35-38% faster, 28672->8192 15-17%
-// rank 0 and 1-30% compensated; with more tiles the unsplit launch fills
+// over 128-row tiles.  Measured at 17..32 tokens (fp16, graph-replayed,
+// against the unsplit launch): 16384->4096 at 32 tokens 26% and 28672->4096
+// 35-38% faster, 28672->8192 15-17% rank 0 and 1-30% compensated (where a
+// split fits, it beats both: 16384->4096 at 17 tokens); with more tiles the unsplit launch fills
 // the chip and stays ahead (16384->16384: wide 15-22% slower, 8192->28672
 // rank 0 13% slower).  The rule reads the layer's shape, rank and M only.
 bool small_decode(const LayerDesc &d, int M) {
